@@ -1,0 +1,241 @@
+"""Throughput of the PISA forward pass on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload wan_bf16]
+
+One step = the whole hot path on one batch: pisa_block_stats, pisa_select and
+pisa_attn_fwd (the fused pass), on seeded synthetic inputs already resident in
+HBM. Prints one JSON line. ``value`` is the effective TFLOP/s of the whole step
+(exact-block + zeroth-order tail + first-order FLOPs over the step time); the
+per-call milliseconds, the fused kernel's roofline fraction, the same-device
+dense baseline and the fp64 CPU oracle's rate on a bounded sample ride along.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "PISA attn fwd ms/call + effective TFLOP/s (%MFMA peak), Wan-shape L=75600 d=0.125"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA peaks
+HBM_PEAK_GBS = 8000.0
+
+
+def flops_from_idx(idx: np.ndarray, L: int, D: int, block: int, first_order: bool) -> dict:
+    """Credited FLOPs of one fused call: 4·D per exact (query, key) pair, 4·D
+    per (query, unselected block) pair, 2·D² per query row of a query block
+    with unselected blocks (hybrid only). Centroid logits of selected blocks,
+    which the kernel computes and masks, are not credited."""
+    B, H, n, k = idx.shape
+    n_last = L - (n - 1) * block
+    nq = np.full(n, block, dtype=np.float64)
+    nq[-1] = n_last
+    has_last = (idx == n - 1).any(axis=-1)                      # [B,H,n]
+    exact_keys = k * block - (block - n_last) * has_last          # Σ_{j∈S_i} n_j
+    exact = float((nq * 4.0 * D * exact_keys).sum())
+    tail = float((nq * 4.0 * D * (n - k)).sum()) * 1.0
+    corr = float(2.0 * D * D * nq.sum() * B * H) if (first_order and k < n) else 0.0
+    return dict(exact=exact, tail=tail, corr=corr, total=exact + tail + corr)
+
+
+def stats_bytes(B, H, L, D, block, esz) -> float:
+    """Algorithmic bytes of the statistics pass: q, k, v read once; operand
+    copies of K and V (2·L·D·esz), block statistics (3·n·D fp64), k̄ and ΣV
+    tiles, per-run partial sums and H̄ written."""
+    n = -(-L // block)
+    bh = B * H
+    read = 3.0 * L * D * esz
+    write = 2.0 * n * block * D * esz + 3.0 * n * D * 8 + 2.0 * (-(-n // 64)) * 64 * D * esz
+    cb = 1024 // block
+    write += (-(-n // cb)) * D * D * 4
+    return bh * (read + write)
+
+
+def cpu_baseline(w, budget_s: float = 15.0) -> dict:
+    """The fp64 oracle on one head: statistics and routing of the whole head,
+    then query blocks one by one until the time budget is spent."""
+    import oracle
+    import synth
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    q, k, v = (synth.as_f64(x) for x in synth.head_tensors(w, 0, 0))
+    n = w.n_blocks
+    topk = oracle.topk_from_density(w.density, n)
+    t0 = time.perf_counter()
+    st = oracle.block_stats(q, k, v, w.block)
+    M = oracle.cov_norm(st["H"], st["Hbar"]) if w.cov_weight else None
+    S = oracle.pooled_scores(st["qbar"], st["kbar"], w.scale, M, w.cov_weight, w.sink_idx)
+    idx = oracle.select_topk(S, topk)
+    t_pre = time.perf_counter() - t0
+    order = np.random.default_rng(0).permutation(n)
+    done = []
+    t1 = time.perf_counter()
+    for i in order:
+        oracle.pisa_rows(q, k, v, st, idx[i], int(i), w.block, w.scale, w.variant == "hyd")
+        done.append(int(i))
+        if time.perf_counter() - t1 > budget_s:
+            break
+    t_rows = time.perf_counter() - t1
+    sizes = oracle.block_sizes(w.L, w.block).astype(np.float64)
+    total = 0.0
+    for i in done:
+        total += sizes[i] * (4.0 * w.D * sizes[idx[i]].sum() + 4.0 * w.D * (n - topk))
+        if w.variant == "hyd" and topk < n:
+            total += 2.0 * sizes[i] * w.D * w.D
+    share = len(done) / n
+    t = t_rows + t_pre * share
+    return {"value": total / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"head (0,0) of {w.name}: statistics + routing of the whole head "
+                      f"({t_pre:.2f}s, charged pro rata), then {len(done)} of {n} query blocks "
+                      f"({t_rows:.1f}s), fp64 NumPy",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="wan_bf16")
+    ap.add_argument("--dense-reps", type=int, default=2)
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path shards over "
+              "(batch, head) with no exchange, so N GPUs run N independent copies.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import block_sparse_attention_stats_amd as bsa
+    import synth
+
+    w = synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
+    q, k, v = synth.make_qkv(w)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    del q, k, v
+    print(f"[bench] inputs on device ({time.time() - t0:.1f}s)", file=sys.stderr, flush=True)
+
+    n = w.n_blocks
+    topk = bsa.topk_from_density(w.density, n)
+    s = w.scale
+    hyd = w.variant == "hyd"
+    shape = bsa.make_shape(qd, w.block)
+    st = bsa.alloc_stats(shape, dev, want_mnorm=w.cov_weight > 0)
+    idx = torch.empty((w.B, w.H, n, topk), dtype=torch.int32, device=dev)
+    o = torch.empty_like(qd)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        bsa.block_stats(qd, kd, vd, w.block, want_mnorm=w.cov_weight > 0, out=st)
+        if ev is not None:
+            ev[1].record()
+        bsa.select(st, topk, s, w.cov_weight, w.sink_idx, out=idx)
+        if ev is not None:
+            ev[2].record()
+        bsa.attn_fwd(qd, st, idx, s, hyd, out=o)
+        if ev is not None:
+            ev[3].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for e in evs:
+        step(e)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    ms = {"block_stats": 0.0, "select": 0.0, "attn_fwd": 0.0}
+    for e in evs:
+        ms["block_stats"] += e[0].elapsed_time(e[1]) / args.steps
+        ms["select"] += e[1].elapsed_time(e[2]) / args.steps
+        ms["attn_fwd"] += e[2].elapsed_time(e[3]) / args.steps
+    ms_step = wall * 1e3 / args.steps
+    ms["total_events"] = sum(ms.values())
+
+    f = flops_from_idx(idx.cpu().numpy(), w.L, w.D, w.block, hyd)
+    fused_tflops = f["total"] / (ms["attn_fwd"] * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    esz = 2 if w.dtype == "bf16" else 4
+    sbytes = stats_bytes(w.B, w.H, w.L, w.D, w.block, esz)
+    print(f"[bench] step {ms_step:.3f} ms: stats {ms['block_stats']:.3f} select {ms['select']:.3f} "
+          f"fused {ms['attn_fwd']:.3f}; fused {fused_tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
+
+    dense = None
+    if not args.no_dense:
+        od = torch.empty_like(qd)
+        ws = torch.empty(bsa.load_library().dense_workspace_bytes(bsa.ctypes.byref(shape)),
+                         dtype=torch.uint8, device=dev)
+        bsa.dense(qd, kd, vd, s, out=od, ws=ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.dense_reps):
+            bsa.dense(qd, kd, vd, s, out=od, ws=ws)
+        e1.record()
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / args.dense_reps
+        dflops = 4.0 * w.B * w.H * float(w.L) * w.L * w.D
+        dense = {"ms": dms, "tflops": dflops / (dms * 1e-3) / 1e12,
+                 "mfma_frac": dflops / (dms * 1e-3) / 1e12 / peak,
+                 "speedup_vs_pisa_step": dms / ms_step, "speedup_vs_pisa_fused": dms / ms["attn_fwd"]}
+        print(f"[bench] dense {dms:.2f} ms, {dense['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del od, ws
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(w, args.cpu_budget)
+
+    out = {
+        "metric": METRIC,
+        "value": f["total"] / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: seeded clustered-Gaussian q/k (64-token clusters), N(0,1) v",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "D": w.D, "block": w.block,
+                   "density": w.density, "topk": topk, "variant": w.variant, "sink_idx": w.sink_idx,
+                   "cov_weight": w.cov_weight, "seed": w.seed},
+        "ms": ms,
+        "flops": f,
+        "fused_tflops": fused_tflops,
+        "exact_phase_mfma_frac": f["exact"] / (ms["attn_fwd"] * 1e-3) / 1e12 / peak,
+        "stats_gbs": sbytes / (ms["block_stats"] * 1e-3) / 1e9,
+        "stats_hbm_frac": sbytes / (ms["block_stats"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "roofline": {"kernel": "k_pisa_fwd", "bound": "mfma", "achieved": fused_tflops, "peak": peak,
+                     "unit": "TFLOP/s", "frac": fused_tflops / peak, "traffic": None},
+        "dense": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

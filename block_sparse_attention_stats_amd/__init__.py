@@ -1,0 +1,263 @@
+"""PISA piecewise sparse attention forward pass on MI355X (gfx950).
+
+A thin ctypes binding over ``libpisa.so`` (C ABI in ``include/pisa.h``). This
+module only checks and marshals arguments and allocates outputs and workspace
+with torch; every step of the computation runs in the library's HIP kernels on
+torch's current stream. Importing works without a GPU; calling needs the built
+library and a visible gfx950 device, otherwise it raises.
+
+Entry points follow the authors' README (``piecewise_sparse_attention_hyd``,
+``piecewise_sparse_attention_0th``, ``piecewise_sparse_attention`` alias;
+keyword arguments ``density``, ``block_size``, ``sink_idx``), with
+``cov_weight`` (covariance-aware routing weight, gist.science summary,
+"Covariance-Aware Routing") and ``scale`` added. The three steps are also
+exposed one by one: :func:`block_stats`, :func:`select`, :func:`attn_fwd`, and
+the same-device dense baseline :func:`dense`.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libpisa.so")
+
+PISA_OK, PISA_EINVAL, PISA_ENOTSUP, PISA_EHIP = 0, 1, 2, 3
+PISA_F32, PISA_BF16 = 0, 1
+PISA_SINK_NONE = -(2 ** 31)
+EXPORTS = ("pisa_workspace_bytes", "pisa_block_stats", "pisa_select", "pisa_attn_fwd",
+           "dense_workspace_bytes", "dense_attn_fwd", "pisa_status_string", "pisa_last_hip_error")
+
+
+class PisaError(RuntimeError):
+    def __init__(self, status: int, where: str, detail: str = ""):
+        self.status = status
+        super().__init__(f"{where}: {_status_text(status)}{(' (' + detail + ')') if detail else ''}")
+
+
+class Shape(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("block", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+
+
+class StatsStruct(ctypes.Structure):
+    _fields_ = [("qbar", ctypes.c_void_p), ("kbar", ctypes.c_void_p), ("vsum", ctypes.c_void_p),
+                ("hbar", ctypes.c_void_p), ("mnorm", ctypes.c_void_p), ("ws", ctypes.c_void_p),
+                ("ws_bytes", ctypes.c_size_t)]
+
+
+_lib_handle = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads libpisa.so (once). Raises if it has not been built."""
+    global _lib_handle
+    if _lib_handle is not None:
+        return _lib_handle
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m block_sparse_attention_stats_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, D64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_size_t
+    SP, STP = ctypes.POINTER(Shape), ctypes.POINTER(StatsStruct)
+    sig = {
+        "pisa_workspace_bytes": (SZ, [SP]),
+        "dense_workspace_bytes": (SZ, [SP]),
+        "pisa_block_stats": (I32, [SP, P, P, P, STP, P]),
+        "pisa_select": (I32, [SP, STP, D64, D64, I32, I32, P, P]),
+        "pisa_attn_fwd": (I32, [SP, P, STP, I32, P, I32, D64, P, P]),
+        "dense_attn_fwd": (I32, [SP, P, P, P, D64, P, P, SZ, P]),
+        "pisa_status_string": (ctypes.c_char_p, [I32]),
+        "pisa_last_hip_error": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    _lib_handle = lib
+    return lib
+
+
+def _status_text(status: int) -> str:
+    try:
+        return load_library().pisa_status_string(status).decode()
+    except Exception:  # library missing: describe the code ourselves
+        return {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP runtime error"}.get(status, "?")
+
+
+def _check(status: int, where: str):
+    if status != PISA_OK:
+        detail = load_library().pisa_last_hip_error().decode() if status == PISA_EHIP else ""
+        raise PisaError(status, where, detail)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PISA_BF16
+    if t.dtype == torch.float32:
+        return PISA_F32
+    raise TypeError(f"unsupported dtype {t.dtype}: use torch.bfloat16 or torch.float32")
+
+
+def _check_qkv(*ts: torch.Tensor):
+    ref = ts[0]
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if t.dim() != 4:
+            raise ValueError("tensors must be [batch, heads, seq, head_dim]")
+        if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("q, k, v must share shape, dtype and device")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def make_shape(q: torch.Tensor, block_size: int) -> Shape:
+    B, H, L, D = q.shape
+    return Shape(B, H, L, D, block_size, _dtype_code(q))
+
+
+def num_blocks(L: int, block_size: int) -> int:
+    return -(-L // block_size)
+
+
+def topk_from_density(density: float, n: int) -> int:
+    """Exact blocks per query block: clamp(floor(density * n), 1, n), in fp64."""
+    k = int(math.floor(float(density) * float(n)))
+    return max(1, min(n, k))
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+@dataclass
+class Stats:
+    """Block statistics of one call (device tensors) and the workspace they live with."""
+
+    shape: Shape
+    qbar: torch.Tensor   # [B,H,n,D] fp64
+    kbar: torch.Tensor   # [B,H,n,D] fp64
+    vsum: torch.Tensor   # [B,H,n,D] fp64
+    hbar: torch.Tensor   # [B,H,D,D] fp64
+    mnorm: torch.Tensor | None  # [B,H,n] fp64
+    ws: torch.Tensor     # uint8 workspace
+
+    def struct(self) -> StatsStruct:
+        return StatsStruct(self.qbar.data_ptr(), self.kbar.data_ptr(), self.vsum.data_ptr(),
+                           self.hbar.data_ptr(), self.mnorm.data_ptr() if self.mnorm is not None else None,
+                           self.ws.data_ptr(), self.ws.numel())
+
+
+def workspace_bytes(shape: Shape) -> int:
+    nbytes = load_library().pisa_workspace_bytes(ctypes.byref(shape))
+    if nbytes == 0:
+        raise PisaError(PISA_EINVAL, "pisa_workspace_bytes")
+    return nbytes
+
+
+def alloc_stats(shape: Shape, device, want_mnorm: bool) -> Stats:
+    B, H, L, D, blk = shape.B, shape.H, shape.L, shape.D, shape.block
+    n = num_blocks(L, blk)
+    f64 = dict(dtype=torch.float64, device=device)
+    ws = torch.empty(workspace_bytes(shape), dtype=torch.uint8, device=device)
+    return Stats(shape, torch.empty((B, H, n, D), **f64), torch.empty((B, H, n, D), **f64),
+                 torch.empty((B, H, n, D), **f64), torch.empty((B, H, D, D), **f64),
+                 torch.empty((B, H, n), **f64) if want_mnorm else None, ws)
+
+
+def block_stats(q, k, v, block_size: int = 64, want_mnorm: bool = False, out: Stats | None = None) -> Stats:
+    """Step 1: q̄, k̄, ΣV, H̄ (and M_j when ``want_mnorm``) via pisa_block_stats."""
+    _check_qkv(q, k, v)
+    shape = make_shape(q, block_size)
+    st = out if out is not None else alloc_stats(shape, q.device, want_mnorm)
+    sst = st.struct()
+    _check(load_library().pisa_block_stats(ctypes.byref(shape), q.data_ptr(), k.data_ptr(),
+                                           v.data_ptr(), ctypes.byref(sst), _stream()),
+           "pisa_block_stats")
+    return st
+
+
+def _sink_code(sink_idx) -> int:
+    if sink_idx is None:
+        return PISA_SINK_NONE
+    if sink_idx in (0, -1):
+        return int(sink_idx)
+    raise ValueError("sink_idx must be None, 0 or -1")
+
+
+def select(st: Stats, topk: int, scale: float, cov_weight: float = 0.0, sink_idx=None,
+           out: torch.Tensor | None = None) -> torch.Tensor:
+    """Step 2: per-query-block top-k key blocks, ascending, [B,H,n,topk] int32."""
+    shape = st.shape
+    n = num_blocks(shape.L, shape.block)
+    idx = out if out is not None else torch.empty((shape.B, shape.H, n, topk), dtype=torch.int32,
+                                                  device=st.qbar.device)
+    sst = st.struct()
+    _check(load_library().pisa_select(ctypes.byref(shape), ctypes.byref(sst), float(scale),
+                                      float(cov_weight), int(topk), _sink_code(sink_idx),
+                                      idx.data_ptr(), _stream()), "pisa_select")
+    return idx
+
+
+def attn_fwd(q, st: Stats, idx: torch.Tensor, scale: float, first_order: bool = True,
+             out: torch.Tensor | None = None) -> torch.Tensor:
+    """Step 3: fused exact + zeroth-order (+ global first-order) pass."""
+    _check_qkv(q)
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or not idx.is_cuda:
+        raise ValueError("idx must be a contiguous int32 GPU tensor")
+    shape = st.shape
+    o = out if out is not None else torch.empty_like(q)
+    sst = st.struct()
+    _check(load_library().pisa_attn_fwd(ctypes.byref(shape), q.data_ptr(), ctypes.byref(sst),
+                                        1 if first_order else 0, idx.data_ptr(), int(idx.shape[-1]),
+                                        float(scale), o.data_ptr(), _stream()), "pisa_attn_fwd")
+    return o
+
+
+def dense(q, k, v, scale: float | None = None, out: torch.Tensor | None = None,
+          ws: torch.Tensor | None = None) -> torch.Tensor:
+    """Same-device dense attention baseline, softmax(scale·QKᵀ)V."""
+    _check_qkv(q, k, v)
+    shape = make_shape(q, 64)
+    s = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
+    lib = load_library()
+    nbytes = lib.dense_workspace_bytes(ctypes.byref(shape))
+    if nbytes == 0:
+        raise PisaError(PISA_EINVAL, "dense_workspace_bytes")
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    o = out if out is not None else torch.empty_like(q)
+    _check(lib.dense_attn_fwd(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(), float(s),
+                              o.data_ptr(), ws.data_ptr(), ws.numel(), _stream()), "dense_attn_fwd")
+    return o
+
+
+def piecewise_sparse_attention_hyd(q, k, v, density: float = 0.15, block_size: int = 64,
+                                   sink_idx=None, cov_weight: float = 0.0, scale=None,
+                                   first_order: bool = True, return_idx: bool = False):
+    """PISA forward (hybrid order: zeroth order + global first-order correction)."""
+    _check_qkv(q, k, v)
+    B, H, L, D = q.shape
+    s = 1.0 / math.sqrt(D) if scale is None else float(scale)
+    n = num_blocks(L, block_size)
+    topk = topk_from_density(density, n)
+    st = block_stats(q, k, v, block_size, want_mnorm=cov_weight > 0)
+    idx = select(st, topk, s, cov_weight, sink_idx)
+    o = attn_fwd(q, st, idx, s, first_order)
+    return (o, idx) if return_idx else o
+
+
+def piecewise_sparse_attention_0th(q, k, v, density: float = 0.15, block_size: int = 64,
+                                   sink_idx=None, cov_weight: float = 0.0, scale=None,
+                                   return_idx: bool = False):
+    """PISA forward, zeroth-order-only variant (no global first-order term)."""
+    return piecewise_sparse_attention_hyd(q, k, v, density, block_size, sink_idx, cov_weight, scale,
+                                          first_order=False, return_idx=return_idx)
+
+
+piecewise_sparse_attention = piecewise_sparse_attention_hyd

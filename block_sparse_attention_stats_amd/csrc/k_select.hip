@@ -1,0 +1,175 @@
+// Per-query-block top-k routing (gist.science technical summary of arXiv
+// 2602.01077, section 2 "Covariance-Aware Routing"; the authors' README,
+// "Attention sink for MMDiT").
+//
+// k_scores: S_ij = scale * q̄_i·k̄_j + cov_weight * M_j in fp64 for 64x64 tiles
+//   of (query block, key block) pairs, a register-tiled fp64 GEMM through LDS
+//   (n x n x D per head: small next to the fused pass). The sink column gets
+//   +infinity.
+// k_topk: one workgroup per score row, held in LDS as order-preserving 64-bit
+//   keys; an MSB-first radix select (8 passes of 8 bits) finds the k-th largest
+//   key T, then two block scans take every key > T and the lowest-index keys
+//   equal to T, and emit the indices ascending.
+#include "pisa_dev.h"
+#include "pisa_internal.h"
+
+namespace pisa {
+
+template <int D>
+__global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
+  __shared__ double As[16][65], Bs[16][65];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const long bh = blockIdx.z;
+  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const double* qb = a.qbar + (size_t)bh * a.n * D;
+  const double* kb = a.kbar + (size_t)bh * a.n * D;
+  double acc[4][4];
+#pragma unroll
+  for (int x = 0; x < 4; ++x)
+#pragma unroll
+    for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
+  for (int d0 = 0; d0 < D; d0 += 16) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int x = tid + 256 * u, row = x >> 4, dd = x & 15;
+      As[dd][row] = (i0 + row < a.n) ? qb[(size_t)(i0 + row) * D + d0 + dd] : 0.0;
+      Bs[dd][row] = (j0 + row < a.n) ? kb[(size_t)(j0 + row) * D + d0 + dd] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int dd = 0; dd < 16; ++dd) {
+      double av[4], bv[4];
+#pragma unroll
+      for (int x = 0; x < 4; ++x) av[x] = As[dd][ty + 16 * x];
+#pragma unroll
+      for (int y = 0; y < 4; ++y) bv[y] = Bs[dd][tx + 16 * y];
+#pragma unroll
+      for (int x = 0; x < 4; ++x)
+#pragma unroll
+        for (int y = 0; y < 4; ++y) acc[x][y] = fma(av[x], bv[y], acc[x][y]);
+    }
+    __syncthreads();
+  }
+  double* out = a.scores + (size_t)bh * a.n * a.n;
+#pragma unroll
+  for (int y = 0; y < 4; ++y) {
+    const int j = j0 + tx + 16 * y;
+    if (j >= a.n) continue;
+    const double cov = a.cov_weight != 0.0 ? a.cov_weight * a.mnorm[bh * a.n + j] : 0.0;
+#pragma unroll
+    for (int x = 0; x < 4; ++x) {
+      const int i = i0 + ty + 16 * x;
+      if (i >= a.n) continue;
+      double sc = a.scale * acc[x][y];
+      if (a.cov_weight != 0.0) sc = sc + cov;
+      if (j == a.sink_block) sc = __builtin_huge_val();
+      out[(size_t)i * a.n + j] = sc;
+    }
+  }
+}
+
+// Monotone map from fp64 to uint64: larger value -> larger key (-0 == +0).
+__device__ inline unsigned long long order_key(double x) {
+  if (x == 0.0) x = 0.0;
+  const unsigned long long u = __double_as_longlong(x);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+
+// Inclusive prefix sum over the 256 threads of the block.
+__device__ inline int block_scan_incl(int v, int* wsum) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(v, o);
+    if (lane >= o) v += y;
+  }
+  __syncthreads();
+  if (lane == 63) wsum[wv] = v;
+  __syncthreads();
+  for (int w = 0; w < wv; ++w) v += wsum[w];
+  return v;
+}
+
+__global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
+  extern __shared__ unsigned long long keys[];
+  __shared__ int hist[256];
+  __shared__ int wsum[4];
+  __shared__ int pick_digit, pick_gt;
+  const int tid = threadIdx.x;
+  const long row = blockIdx.x;
+  const int n = a.n, k = a.topk;
+  int32_t* out = a.idx + row * (long)k;
+  if (k >= n) {
+    for (int j = tid; j < n; j += 256) out[j] = j;
+    return;
+  }
+  const double* S = a.scores + row * (long)n;
+  for (int j = tid; j < n; j += 256) keys[j] = order_key(S[j]);
+
+  unsigned long long prefix = 0, pmask = 0;
+  int kk = k;
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    hist[tid] = 0;
+    __syncthreads();
+    for (int j = tid; j < n; j += 256) {
+      const unsigned long long key = keys[j];
+      if ((key & pmask) == prefix) atomicAdd(&hist[(int)((key >> shift) & 255)], 1);
+    }
+    __syncthreads();
+    // thread t looks at digit 255 - t: incl = count of candidates with digit >= it
+    const int dg = 255 - tid;
+    const int c = hist[dg];
+    const int incl = block_scan_incl(c, wsum);
+    const int gt = incl - c;
+    if (gt < kk && kk <= incl) {
+      pick_digit = dg;
+      pick_gt = gt;
+    }
+    __syncthreads();
+    prefix |= (unsigned long long)pick_digit << shift;
+    pmask |= 255ull << shift;
+    kk -= pick_gt;
+    __syncthreads();
+  }
+  // prefix = T, the k-th largest key; take all keys > T and the kk lowest-index keys == T
+  const int per = (n + 255) / 256, lo = min(n, tid * per), hi = min(n, lo + per);
+  int ceq = 0;
+  for (int j = lo; j < hi; ++j) ceq += (keys[j] == prefix);
+  int eq_before = block_scan_incl(ceq, wsum) - ceq;
+  int cnt = 0;
+  {
+    int r = eq_before;
+    for (int j = lo; j < hi; ++j) {
+      const unsigned long long key = keys[j];
+      const bool sel = key > prefix || (key == prefix && r++ < kk);
+      cnt += sel;
+    }
+  }
+  int pos = block_scan_incl(cnt, wsum) - cnt;
+  {
+    int r = eq_before;
+    for (int j = lo; j < hi; ++j) {
+      const unsigned long long key = keys[j];
+      const bool sel = key > prefix || (key == prefix && r++ < kk);
+      if (sel) out[pos++] = j;
+    }
+  }
+}
+
+hipError_t launch_scores(int D, const ScoreArgs& a, long bh, hipStream_t s) {
+  const unsigned t = (unsigned)((a.n + 63) / 64);
+  dim3 grid(t, t, (unsigned)bh);
+  if (D == 64)
+    hipLaunchKernelGGL((k_scores<64>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_scores<128>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const TopkArgs& a, long rows, hipStream_t s) {
+  const size_t lds = (size_t)a.n * sizeof(unsigned long long);
+  hipLaunchKernelGGL(k_topk, dim3((unsigned)rows), dim3(256), lds, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pisa

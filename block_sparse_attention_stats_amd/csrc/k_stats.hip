@@ -1,0 +1,322 @@
+// Block statistics (PISA pre-computation; gist.science technical summary of
+// arXiv 2602.01077, section 2 "Hardware Implementation" step 1, symbols of
+// "Core Algorithm"): for every block j of a (batch, head)
+//   q̄_j = mean of its query rows, k̄_j = mean of its keys, ΣV_j = Σ v,
+//   H_j = Σ_n (k_n − k̄_j)ᵀ v_n, and H̄ = (1/n) Σ_j H_j;
+// optionally M_j = ||H_j − H̄||_F ("Covariance-Aware Routing").
+//
+// One HBM-streaming pass: each workgroup walks a run of consecutive blocks of
+// one head, staging 64-token sub-tiles of q, k, v through LDS (the next
+// sub-tile is already loading while the current one is consumed). Per
+// sub-tile it
+//   * sums columns in fp64 (exact for bf16/fp32 inputs of one block),
+//   * writes K and V in the operand order of the fused kernel (K-format and
+//     V-format sub-tiles, see pisa_dev.h) so that kernel reads them with
+//     whole-wavefront 1 KiB loads,
+//   * accumulates G = Kᵀ V on MFMA (bf16 products are exact in fp32) and
+//     subtracts k̄_j ⊗ ΣV_j once block j is complete, leaving Σ_j H_j of the
+//     run in the accumulators; runs are summed in fp64 by k_hbar_reduce.
+#include "pisa_dev.h"
+#include "pisa_internal.h"
+
+namespace pisa {
+
+template <typename T, int D, int MODE>
+__global__ __launch_bounds__(256) void k_block_stats(StatsArgs a) {
+  using G = Geo<T, D>;
+  using O = Op<T>;
+  constexpr int KW = G::KW, ESZ = G::ESZ, CPR = G::CPR, NC = G::NC, DT = G::DT, CPK = G::CPK;
+  constexpr int PITCH = G::ROW_BYTES + 16;  // padded LDS row: transposed reads spread over banks
+  constexpr int NT = (MODE == kStatsFull) ? 3 : 2;
+  constexpr int PER = 64 * CPR / 256;       // 16-byte chunks per thread per tensor per sub-tile
+  constexpr int TW = DT / 2;                // G tiles per side per wave (2x2 waves)
+  constexpr int KT = NT - 2, VT = NT - 1;   // LDS slots of k and v
+  constexpr bool kDoG = (MODE != kStatsPackOnly);
+  constexpr bool kDoPack = (MODE != kStatsMnorm);
+  static_assert(PER >= 1 && TW >= 1, "shape");
+
+  __shared__ __align__(16) uint8_t tile[NT][64 * PITCH];
+  __shared__ float kbf[D], vsf[D];
+  __shared__ double kbd[D], vsd[D];
+  __shared__ double red[4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const long bh = blockIdx.x / a.nch;
+  const int ch = (int)(blockIdx.x % a.nch);
+  const int j0 = ch * a.cb, j1 = min(a.n, j0 + a.cb);
+  const int spb = a.blk / kSub;
+  const int total_sub = (j1 - j0) * spb;
+  const uint8_t* src[NT];
+  if constexpr (MODE == kStatsFull) {
+    src[0] = a.q; src[1] = a.k; src[2] = a.v;
+  } else {
+    src[0] = a.k; src[1] = a.v;
+  }
+  const size_t head_bytes = (size_t)a.L * G::ROW_BYTES;
+
+  // G tiles owned by this wave: rows d in tiles dt0.., columns e in tiles et0..
+  const int dt0 = TW * (wv >> 1), et0 = TW * (wv & 1);
+  f32x16 acc[TW][TW];
+#pragma unroll
+  for (int x = 0; x < TW; ++x)
+#pragma unroll
+    for (int y = 0; y < TW; ++y) acc[x][y] = f32x16{};
+
+  double hb[TW][TW][16];  // H̄ entries of the owned tiles (mnorm pass)
+  if constexpr (MODE == kStatsMnorm) {
+#pragma unroll
+    for (int x = 0; x < TW; ++x)
+#pragma unroll
+      for (int y = 0; y < TW; ++y)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int d = 32 * (dt0 + x) + vkey(r, h), e = 32 * (et0 + y) + l32;
+          hb[x][y][r] = a.hbar[(bh * D + d) * D + e];
+        }
+  }
+
+  double csum[2] = {0.0, 0.0};  // column-sum tasks p = tid, tid + 256 over (tensor, d)
+
+  uint4 pre[NT][PER];
+  auto load_sub = [&](int s) {
+    const int j = j0 + s / spb, st = s % spb;
+    const int r0 = j * a.blk + st * kSub;
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int x = tid + 256 * i, row = x / CPR, cc = x % CPR;
+        const int grow = r0 + row;
+        if (grow < a.L)
+          pre[t][i] = *(const uint4*)(src[t] + bh * head_bytes + (size_t)grow * G::ROW_BYTES + cc * 16);
+        else
+          pre[t][i] = make_uint4(0, 0, 0, 0);
+      }
+  };
+
+  if (total_sub > 0) load_sub(0);
+  for (int s = 0; s < total_sub; ++s) {
+    const int j = j0 + s / spb, st = s % spb;
+    __syncthreads();  // LDS free
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int x = tid + 256 * i, row = x / CPR, cc = x % CPR;
+        *(uint4*)(&tile[t][row * PITCH + cc * 16]) = pre[t][i];
+      }
+    if constexpr (MODE == kStatsMnorm) {
+      if (st == 0)
+        for (int d = tid; d < D; d += 256) {
+          kbd[d] = a.kbar[(bh * a.n + j) * D + d];
+          vsd[d] = a.vsum[(bh * a.n + j) * D + d];
+        }
+    }
+    __syncthreads();
+    if (s + 1 < total_sub) load_sub(s + 1);
+
+    // ---- fp64 column sums (q, k, v)
+    if constexpr (MODE == kStatsFull) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int p = tid + 256 * u;
+        if (p < 3 * D) {
+          const int t = p / D, d = p % D;
+          double sacc = 0.0;
+          for (int row = 0; row < 64; ++row)
+            sacc += (double)O::to_f32(*(const T*)(&tile[t][row * PITCH + d * ESZ]));
+          csum[u] += sacc;
+        }
+      }
+    }
+
+    // ---- operand-ordered copies of K and V
+    if constexpr (kDoPack) {
+      const size_t sub_idx = ((size_t)bh * a.n + j) * spb + st;
+      uint8_t* kdst = a.kp + sub_idx * G::SUB_BYTES;
+      uint8_t* vdst = a.vp + sub_idx * G::SUB_BYTES;
+#pragma unroll
+      for (int i = 0; i < NC / 2; ++i) {
+        const int u = tid + 256 * i, ul = u & 63, wc = u >> 6;
+        const int w = wc / NC, c = wc % NC;
+        const int kk = 32 * w + (ul & 31), d0 = 2 * KW * c + KW * (ul >> 5);
+        *(uint4*)(kdst + (size_t)u * 16) = *(const uint4*)(&tile[KT][kk * PITCH + d0 * ESZ]);
+      }
+#pragma unroll
+      for (int i = 0; i < DT * CPK / 2; ++i) {
+        const int u = tid + 256 * i, ul = u & 63, ci = u >> 6;
+        const int w = ci / (DT * CPK), rem = ci % (DT * CPK), dt = rem / CPK, c = rem % CPK;
+        const int d = 32 * dt + (ul & 31), hh = ul >> 5;
+        T vals[KW];
+#pragma unroll
+        for (int e = 0; e < KW; ++e)
+          vals[e] = *(const T*)(&tile[VT][(32 * w + vkey(KW * c + e, hh)) * PITCH + d * ESZ]);
+        *(uint4*)(vdst + (size_t)u * 16) = __builtin_bit_cast(uint4, vals);
+      }
+    }
+
+    // ---- G += Kᵀ V on MFMA (contraction over the 64 tokens of the sub-tile)
+    if constexpr (kDoG) {
+#pragma unroll
+      for (int w = 0; w < 2; ++w)
+#pragma unroll
+        for (int c = 0; c < CPK; ++c) {
+          uint4 A[TW], B[TW];
+#pragma unroll
+          for (int x = 0; x < TW; ++x) {
+            T av[KW], bv[KW];
+            const int dA = 32 * (dt0 + x) + l32, dB = 32 * (et0 + x) + l32;
+#pragma unroll
+            for (int e = 0; e < KW; ++e) {
+              const int row = (32 * w + vkey(KW * c + e, h)) * PITCH;
+              av[e] = *(const T*)(&tile[KT][row + dA * ESZ]);
+              bv[e] = *(const T*)(&tile[VT][row + dB * ESZ]);
+            }
+            A[x] = __builtin_bit_cast(uint4, av);
+            B[x] = __builtin_bit_cast(uint4, bv);
+          }
+#pragma unroll
+          for (int x = 0; x < TW; ++x)
+#pragma unroll
+            for (int y = 0; y < TW; ++y) O::mma(acc[x][y], A[x], B[y]);
+        }
+    }
+
+    if (st != spb - 1) continue;
+    // ---- block j complete
+    const int nj = min(a.blk, a.L - j * a.blk);
+    if constexpr (MODE == kStatsFull) {
+      const int ct = j >> 6, kk = j & 63;
+      uint8_t* kb_tile = a.kbp + ((size_t)bh * a.nct + ct) * G::SUB_BYTES;
+      uint8_t* vb_tile = a.vbp + ((size_t)bh * a.nct + ct) * G::SUB_BYTES;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int p = tid + 256 * u;
+        if (p < 3 * D) {
+          const int t = p / D, d = p % D;
+          const size_t o = ((size_t)bh * a.n + j) * D + d;
+          if (t == 0) {
+            a.qbar[o] = csum[u] / nj;
+          } else if (t == 1) {
+            const double kb = csum[u] / nj;
+            a.kbar[o] = kb;
+            kbf[d] = (float)kb;
+            *(T*)(kb_tile + kfmt_offset<T, D>(kk, d)) = O::from_f32((float)kb);
+          } else {
+            a.vsum[o] = csum[u];
+            vsf[d] = (float)csum[u];
+            *(T*)(vb_tile + vfmt_offset<T, D>(kk, d)) = O::from_f32((float)csum[u]);
+          }
+          csum[u] = 0.0;
+        }
+      }
+      __syncthreads();
+      // Σ_n (k_n − k̄_j)ᵀ v_n = G_j − k̄_j ⊗ ΣV_j
+#pragma unroll
+      for (int x = 0; x < TW; ++x)
+#pragma unroll
+        for (int y = 0; y < TW; ++y)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            acc[x][y][r] -= kbf[32 * (dt0 + x) + vkey(r, h)] * vsf[32 * (et0 + y) + l32];
+    } else if constexpr (MODE == kStatsMnorm) {
+      double ss = 0.0;
+#pragma unroll
+      for (int x = 0; x < TW; ++x)
+#pragma unroll
+        for (int y = 0; y < TW; ++y)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int d = 32 * (dt0 + x) + vkey(r, h), e = 32 * (et0 + y) + l32;
+            const double diff = (double)acc[x][y][r] - kbd[d] * vsd[e] - hb[x][y][r];
+            ss += diff * diff;
+            acc[x][y][r] = 0.0f;
+          }
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+      if (lane == 0) red[wv] = ss;
+      __syncthreads();
+      if (tid == 0) a.mnorm[bh * a.n + j] = sqrt(red[0] + red[1] + red[2] + red[3]);
+    }
+  }
+
+  if constexpr (MODE == kStatsFull) {
+    float* dst = a.hpart + ((size_t)bh * a.nch + ch) * D * D;
+#pragma unroll
+    for (int x = 0; x < TW; ++x)
+#pragma unroll
+      for (int y = 0; y < TW; ++y)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int d = 32 * (dt0 + x) + vkey(r, h), e = 32 * (et0 + y) + l32;
+          dst[d * D + e] = acc[x][y][r];
+        }
+  }
+}
+
+// H̄ = (1/n) Σ_runs (Σ_j H_j), summed in fp64; writes H̄ (fp64), its operand
+// chunks for the fused kernel, and zeroes the padding rows of the k̄ / ΣV tiles.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void k_hbar_reduce(StatsArgs a) {
+  using G = Geo<T, D>;
+  using O = Op<T>;
+  constexpr int KW = G::KW, NC = G::NC;
+  const long bh = blockIdx.x;
+  const int x = blockIdx.y * 256 + threadIdx.x;
+  if (x < D * D) {
+    const int d = x / D, e = x % D;
+    double s = 0.0;
+    for (int c = 0; c < a.nch; ++c) s += (double)a.hpart[(((size_t)bh * a.nch + c) * D + d) * D + e];
+    const double hbv = s / a.n;
+    a.hbar[(bh * D + d) * D + e] = hbv;
+    const int et = e >> 5, lane = ((d % (2 * KW)) / KW) * 32 + (e & 31), c = d / (2 * KW), ee = d % KW;
+    T* hbt = (T*)(a.hbt + (size_t)bh * D * D * G::ESZ);
+    hbt[((et * NC + c) * kWave + lane) * KW + ee] = O::from_f32((float)hbv);
+  }
+  if (blockIdx.y == 0) {
+    const int pad = a.nct * 64 - a.n;
+    const int ct = a.nct - 1;
+    uint8_t* kb_tile = a.kbp + ((size_t)bh * a.nct + ct) * G::SUB_BYTES;
+    uint8_t* vb_tile = a.vbp + ((size_t)bh * a.nct + ct) * G::SUB_BYTES;
+    for (int y = threadIdx.x; y < pad * D; y += 256) {
+      const int kk = (a.n & 63) + y / D, d = y % D;
+      *(T*)(kb_tile + kfmt_offset<T, D>(kk, d)) = O::from_f32(0.0f);
+      *(T*)(vb_tile + vfmt_offset<T, D>(kk, d)) = O::from_f32(0.0f);
+    }
+  }
+}
+
+template <typename T, int D>
+static hipError_t launch_stats_t(int mode, const StatsArgs& a, long bh, hipStream_t s) {
+  dim3 grid((unsigned)(bh * a.nch));
+  if (mode == kStatsFull)
+    hipLaunchKernelGGL((k_block_stats<T, D, kStatsFull>), grid, dim3(256), 0, s, a);
+  else if (mode == kStatsMnorm)
+    hipLaunchKernelGGL((k_block_stats<T, D, kStatsMnorm>), grid, dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((k_block_stats<T, D, kStatsPackOnly>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_stats(int dtype, int D, int mode, const StatsArgs& a, long bh,
+                              hipStream_t s) {
+  if (dtype == 1) return D == 64 ? launch_stats_t<bf16, 64>(mode, a, bh, s)
+                                 : launch_stats_t<bf16, 128>(mode, a, bh, s);
+  return D == 64 ? launch_stats_t<float, 64>(mode, a, bh, s)
+                 : launch_stats_t<float, 128>(mode, a, bh, s);
+}
+
+template <typename T, int D>
+static hipError_t launch_reduce_t(const StatsArgs& a, long bh, hipStream_t s) {
+  dim3 grid((unsigned)bh, (unsigned)((D * D + 255) / 256));
+  hipLaunchKernelGGL((k_hbar_reduce<T, D>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_hbar_reduce(int dtype, int D, const StatsArgs& a, long bh, hipStream_t s) {
+  if (dtype == 1) return D == 64 ? launch_reduce_t<bf16, 64>(a, bh, s)
+                                 : launch_reduce_t<bf16, 128>(a, bh, s);
+  return D == 64 ? launch_reduce_t<float, 64>(a, bh, s) : launch_reduce_t<float, 128>(a, bh, s);
+}
+
+}  // namespace pisa

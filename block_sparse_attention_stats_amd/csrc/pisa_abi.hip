@@ -1,0 +1,243 @@
+// C ABI of the PISA forward pass: argument validation, workspace layout and
+// launch order. Every check runs before anything is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/pisa.h"
+#include "pisa_internal.h"
+
+#define PISA_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_hip_error[256] = "";
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Validates the shape; fills the workspace layout. Returns PISA_OK or the error.
+pisa_status_t check_shape(const pisa_shape_t* s, pisa::WsLayout* w) {
+  if (s == nullptr) return PISA_EINVAL;
+  if (s->B < 1 || s->H < 1 || s->L < 1 || s->D < 1 || s->block < 1) return PISA_EINVAL;
+  if (s->dtype != PISA_F32 && s->dtype != PISA_BF16) return PISA_EINVAL;
+  if (s->D != 64 && s->D != 128) return PISA_ENOTSUP;
+  if (s->block != 64 && s->block != 128) return PISA_ENOTSUP;
+  const long bh = (long)s->B * s->H;
+  const long n = ((long)s->L + s->block - 1) / s->block;
+  if (n > pisa::kMaxBlocks) return PISA_ENOTSUP;
+  if (bh > (1L << 24)) return PISA_ENOTSUP;  // grid sizes stay far inside 2^31
+  if (bh * n * (s->block / 64) > (1L << 30)) return PISA_ENOTSUP;
+  if (w == nullptr) return PISA_OK;
+  const int esz = s->dtype == PISA_BF16 ? 2 : 4;
+  w->bh = bh;
+  w->n = (int)n;
+  w->spb = s->block / 64;
+  w->nct = (int)((n + 63) / 64);
+  w->cb = 1024 / s->block;
+  w->nch = (int)((n + w->cb - 1) / w->cb);
+  w->esz = esz;
+  const size_t sub = (size_t)64 * s->D * esz;
+  size_t off = 0;
+  w->kp = off;
+  off = align256(off + (size_t)bh * n * w->spb * sub);
+  w->vp = off;
+  off = align256(off + (size_t)bh * n * w->spb * sub);
+  w->dense_total = off;
+  w->kbp = off;
+  off = align256(off + (size_t)bh * w->nct * sub);
+  w->vbp = off;
+  off = align256(off + (size_t)bh * w->nct * sub);
+  w->hbt = off;
+  off = align256(off + (size_t)bh * s->D * s->D * esz);
+  w->hpart = off;
+  off = align256(off + (size_t)bh * w->nch * s->D * s->D * sizeof(float));
+  w->scores = off;
+  off = align256(off + (size_t)bh * n * n * sizeof(double));
+  w->total = off;
+  return PISA_OK;
+}
+
+pisa_status_t check_stats(const pisa_stats_t* st, const pisa::WsLayout& w, bool need_mnorm) {
+  if (st == nullptr) return PISA_EINVAL;
+  const double* p[] = {st->qbar, st->kbar, st->vsum, st->hbar};
+  for (const double* x : p)
+    if (x == nullptr || !aligned(x, 8)) return PISA_EINVAL;
+  if (need_mnorm && st->mnorm == nullptr) return PISA_EINVAL;
+  if (st->mnorm != nullptr && !aligned(st->mnorm, 8)) return PISA_EINVAL;
+  if (st->ws == nullptr || !aligned(st->ws, 256) || st->ws_bytes < w.total) return PISA_EINVAL;
+  return PISA_OK;
+}
+
+bool tensor_ok(const void* p) { return p != nullptr && aligned(p, 16); }
+
+pisa_status_t hip_status(hipError_t e) {
+  if (e == hipSuccess) return PISA_OK;
+  strncpy(g_last_hip_error, hipGetErrorString(e), sizeof(g_last_hip_error) - 1);
+  g_last_hip_error[sizeof(g_last_hip_error) - 1] = '\0';
+  return PISA_EHIP;
+}
+
+pisa::StatsArgs stats_args(const pisa_shape_t* s, const pisa::WsLayout& w, const void* q,
+                           const void* k, const void* v, const pisa_stats_t* st, void* ws) {
+  pisa::StatsArgs a;
+  uint8_t* base = (uint8_t*)ws;
+  a.q = (const uint8_t*)q;
+  a.k = (const uint8_t*)k;
+  a.v = (const uint8_t*)v;
+  a.qbar = st ? st->qbar : nullptr;
+  a.kbar = st ? st->kbar : nullptr;
+  a.vsum = st ? st->vsum : nullptr;
+  a.mnorm = st ? st->mnorm : nullptr;
+  a.hbar = st ? st->hbar : nullptr;
+  a.kp = base + w.kp;
+  a.vp = base + w.vp;
+  a.kbp = base + w.kbp;
+  a.vbp = base + w.vbp;
+  a.hbt = base + w.hbt;
+  a.hpart = (float*)(base + w.hpart);
+  a.L = s->L;
+  a.n = w.n;
+  a.blk = s->block;
+  a.cb = w.cb;
+  a.nch = w.nch;
+  a.nct = w.nct;
+  return a;
+}
+
+pisa::FwdArgs fwd_args(const pisa_shape_t* s, const pisa::WsLayout& w, const void* q, void* o,
+                       void* ws, const int32_t* idx, int topk, double scale, int first_order,
+                       int tail) {
+  pisa::FwdArgs a;
+  uint8_t* base = (uint8_t*)ws;
+  a.q = (const uint8_t*)q;
+  a.o = (uint8_t*)o;
+  a.kp = base + w.kp;
+  a.vp = base + w.vp;
+  a.kbp = base + w.kbp;
+  a.vbp = base + w.vbp;
+  a.hbt = base + w.hbt;
+  a.idx = idx;
+  a.total = w.bh * w.n * w.spb;
+  a.per_xcd = (a.total + pisa::kNumXcd - 1) / pisa::kNumXcd;
+  a.L = s->L;
+  a.n = w.n;
+  a.blk = s->block;
+  a.topk = topk;
+  a.n_last = s->L - (w.n - 1) * s->block;
+  a.nct = w.nct;
+  a.cs = (float)(scale * 1.4426950408889634);
+  a.scale = (float)scale;
+  a.first_order = first_order;
+  a.tail = tail;
+  return a;
+}
+
+}  // namespace
+
+PISA_API size_t pisa_workspace_bytes(const pisa_shape_t* shape) {
+  pisa::WsLayout w;
+  return check_shape(shape, &w) == PISA_OK ? w.total : 0;
+}
+
+PISA_API size_t dense_workspace_bytes(const pisa_shape_t* shape) {
+  pisa::WsLayout w;
+  return check_shape(shape, &w) == PISA_OK ? w.dense_total : 0;
+}
+
+PISA_API pisa_status_t pisa_block_stats(const pisa_shape_t* shape, const void* q, const void* k,
+                                        const void* v, const pisa_stats_t* st, void* stream) {
+  pisa::WsLayout w;
+  pisa_status_t rc = check_shape(shape, &w);
+  if (rc != PISA_OK) return rc;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v)) return PISA_EINVAL;
+  if ((rc = check_stats(st, w, false)) != PISA_OK) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  pisa::StatsArgs a = stats_args(shape, w, q, k, v, st, st->ws);
+  if ((rc = hip_status(pisa::launch_block_stats(shape->dtype, shape->D, pisa::kStatsFull, a, w.bh, s))))
+    return rc;
+  if ((rc = hip_status(pisa::launch_hbar_reduce(shape->dtype, shape->D, a, w.bh, s)))) return rc;
+  if (st->mnorm != nullptr)
+    if ((rc = hip_status(pisa::launch_block_stats(shape->dtype, shape->D, pisa::kStatsMnorm, a, w.bh, s))))
+      return rc;
+  return PISA_OK;
+}
+
+PISA_API pisa_status_t pisa_select(const pisa_shape_t* shape, const pisa_stats_t* st, double scale,
+                                   double cov_weight, int32_t topk, int32_t sink_idx, int32_t* idx,
+                                   void* stream) {
+  pisa::WsLayout w;
+  pisa_status_t rc = check_shape(shape, &w);
+  if (rc != PISA_OK) return rc;
+  if (!(scale > 0.0) || !isfinite(scale)) return PISA_EINVAL;
+  if (!(cov_weight >= 0.0) || !isfinite(cov_weight)) return PISA_EINVAL;
+  if (topk < 1 || topk > w.n) return PISA_EINVAL;
+  if (sink_idx != PISA_SINK_NONE && sink_idx != 0 && sink_idx != -1) return PISA_EINVAL;
+  if ((rc = check_stats(st, w, cov_weight > 0.0)) != PISA_OK) return rc;
+  if (idx == nullptr || !aligned(idx, 4)) return PISA_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* base = (uint8_t*)st->ws;
+  pisa::ScoreArgs sa;
+  sa.qbar = st->qbar;
+  sa.kbar = st->kbar;
+  sa.mnorm = st->mnorm;
+  sa.scores = (double*)(base + w.scores);
+  sa.scale = scale;
+  sa.cov_weight = cov_weight;
+  sa.n = w.n;
+  sa.sink_block = sink_idx == PISA_SINK_NONE ? -1 : (sink_idx == 0 ? 0 : w.n - 1);
+  if (topk < w.n)
+    if ((rc = hip_status(pisa::launch_scores(shape->D, sa, w.bh, s)))) return rc;
+  pisa::TopkArgs ta;
+  ta.scores = sa.scores;
+  ta.idx = idx;
+  ta.n = w.n;
+  ta.topk = topk;
+  return hip_status(pisa::launch_topk(ta, w.bh * w.n, s));
+}
+
+PISA_API pisa_status_t pisa_attn_fwd(const pisa_shape_t* shape, const void* q,
+                                     const pisa_stats_t* st, int32_t first_order,
+                                     const int32_t* idx, int32_t topk, double scale, void* o,
+                                     void* stream) {
+  pisa::WsLayout w;
+  pisa_status_t rc = check_shape(shape, &w);
+  if (rc != PISA_OK) return rc;
+  if (!tensor_ok(q) || !tensor_ok(o)) return PISA_EINVAL;
+  if (!(scale > 0.0) || !isfinite(scale)) return PISA_EINVAL;
+  if (first_order != 0 && first_order != 1) return PISA_EINVAL;
+  if (topk < 1 || topk > w.n) return PISA_EINVAL;
+  if (idx == nullptr || !aligned(idx, 4)) return PISA_EINVAL;
+  if ((rc = check_stats(st, w, false)) != PISA_OK) return rc;
+  pisa::FwdArgs a = fwd_args(shape, w, q, o, st->ws, idx, topk, scale, first_order, 1);
+  return hip_status(pisa::launch_fwd(shape->dtype, shape->D, a, (hipStream_t)stream));
+}
+
+PISA_API pisa_status_t dense_attn_fwd(const pisa_shape_t* shape, const void* q, const void* k,
+                                      const void* v, double scale, void* o, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  pisa::WsLayout w;
+  pisa_status_t rc = check_shape(shape, &w);
+  if (rc != PISA_OK) return rc;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o)) return PISA_EINVAL;
+  if (!(scale > 0.0) || !isfinite(scale)) return PISA_EINVAL;
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < w.dense_total) return PISA_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  pisa::StatsArgs sa = stats_args(shape, w, q, k, v, nullptr, ws);
+  if ((rc = hip_status(pisa::launch_block_stats(shape->dtype, shape->D, pisa::kStatsPackOnly, sa, w.bh, s))))
+    return rc;
+  pisa::FwdArgs a = fwd_args(shape, w, q, o, ws, nullptr, w.n, scale, 0, 0);
+  return hip_status(pisa::launch_fwd(shape->dtype, shape->D, a, s));
+}
+
+PISA_API const char* pisa_status_string(pisa_status_t status) {
+  switch (status) {
+    case PISA_OK: return "ok";
+    case PISA_EINVAL: return "invalid argument";
+    case PISA_ENOTSUP: return "unsupported shape or dtype";
+    case PISA_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+PISA_API const char* pisa_last_hip_error(void) { return g_last_hip_error; }

@@ -1,0 +1,70 @@
+// Host-side interface between the C ABI (pisa_abi.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pisa {
+
+// Byte offsets of the regions of the caller's workspace (all 256-aligned).
+struct WsLayout {
+  size_t kp, vp;      // K-format / V-format sub-tiles of K and V: [BH][n][blk/64][64*D]
+  size_t kbp, vbp;    // K-format k̄ / V-format ΣV tiles: [BH][ceil(n/64)][64*D]
+  size_t hbt;         // H̄ᵀ operand chunks: [BH][D*D]
+  size_t hpart;       // fp32 partial Σ_j H_j per chunk of blocks: [BH][nch][D][D]
+  size_t scores;      // fp64 routing scores: [BH][n][n]
+  size_t total;       // bytes needed by stats + select + forward
+  size_t dense_total; // bytes needed by the dense baseline (kp + vp)
+  int n, spb, nct, cb, nch, esz;
+  long bh;
+};
+
+struct StatsArgs {
+  const uint8_t *q, *k, *v;
+  double *qbar, *kbar, *vsum, *mnorm;
+  double* hbar;
+  uint8_t *kp, *vp, *kbp, *vbp, *hbt;
+  float* hpart;
+  int L, n, blk, cb, nch, nct;
+};
+
+struct ScoreArgs {
+  const double *qbar, *kbar, *mnorm;
+  double* scores;
+  double scale, cov_weight;
+  int n, sink_block;  // sink_block < 0: none
+};
+
+struct TopkArgs {
+  const double* scores;
+  int32_t* idx;
+  int n, topk;
+};
+
+struct FwdArgs {
+  const uint8_t* q;
+  uint8_t* o;
+  const uint8_t *kp, *vp, *kbp, *vbp, *hbt;
+  const int32_t* idx;  // nullptr: every key block (dense)
+  long total, per_xcd;
+  int L, n, blk, topk, n_last, nct;
+  float cs;     // scale * log2(e)
+  float scale;
+  int first_order, tail;
+};
+
+enum StatsMode { kStatsFull = 0, kStatsMnorm = 1, kStatsPackOnly = 2 };
+
+// Each returns hipGetLastError() after enqueueing.
+hipError_t launch_block_stats(int dtype, int D, int mode, const StatsArgs& a, long bh,
+                              hipStream_t s);
+hipError_t launch_hbar_reduce(int dtype, int D, const StatsArgs& a, long bh, hipStream_t s);
+hipError_t launch_scores(int D, const ScoreArgs& a, long bh, hipStream_t s);
+hipError_t launch_topk(const TopkArgs& a, long rows, hipStream_t s);
+hipError_t launch_fwd(int dtype, int D, const FwdArgs& a, hipStream_t s);
+
+constexpr int kMaxBlocks = 8192;  // routing keeps one score row per workgroup in LDS
+constexpr int kNumXcd = 8;        // XCDs of an MI355X; workgroups are dealt to them round-robin
+
+}  // namespace pisa

@@ -1,0 +1,141 @@
+/*
+ * pisa.h -- C ABI of the MI355X (gfx950) PISA piecewise sparse attention
+ * forward pass.
+ *
+ * The method (arXiv 2602.01077; gist.science technical summary, section 2
+ * "Methodology", subsections "Core Algorithm", "Covariance-Aware Routing" and
+ * "Hardware Implementation"; the authors' README, "Kernel variants" and
+ * "Attention sink for MMDiT"): per (batch, head), keys and queries are cut into
+ * blocks of `block` tokens. Each query block i attends exactly to the top-k key
+ * blocks S_i chosen from pooled statistics; every other block j (the set U_i)
+ * enters the same softmax numerator and denominator through its zeroth-order
+ * Taylor term at the key centroid, and the hybrid variant adds one global
+ * first-order correction built from the mean first-order matrix H̄:
+ *
+ *   o_t = N_t / D_t,  α_tj = exp(s q_t·k̄_j),
+ *   N_t = Σ_{j∈S_i} Σ_n e^{s q_t·k_n} v_n + Σ_{j∈U_i} α_tj ΣV_j
+ *         + [hybrid] (Σ_{j∈U_i} α_tj) · s · q_t H̄,
+ *   D_t = Σ_{j∈S_i} Σ_n e^{s q_t·k_n} + Σ_{j∈U_i} n_j α_tj.
+ *
+ * Conventions for every entry point:
+ *  - Tensors q, k, v, o are DEVICE pointers to contiguous [B, H, L, D] arrays
+ *    of the I/O dtype, owned by the caller, 16-byte aligned.
+ *  - n = ceil(L / block) blocks per (batch, head); the last one holds
+ *    n_last = L - (n-1)*block tokens.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *    and runs asynchronously; the caller keeps every buffer alive until the
+ *    stream has passed the call. No entry point synchronises the device, and
+ *    the library allocates no device memory: scratch space is the caller's
+ *    workspace.
+ *  - Arguments are validated before anything is enqueued. A bad argument
+ *    returns PISA_EINVAL and enqueues nothing; a combination the library does
+ *    not build returns PISA_ENOTSUP; a launch failure reported by the HIP
+ *    runtime returns PISA_EHIP. No call aborts the process or throws.
+ *  - The library keeps no global state and may be called from several host
+ *    threads at once on different workspaces.
+ */
+#ifndef PISA_H_
+#define PISA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PISA_OK = 0,
+  PISA_EINVAL = 1,  /* invalid argument; nothing enqueued */
+  PISA_ENOTSUP = 2, /* valid but not built (e.g. an unsupported head_dim) */
+  PISA_EHIP = 3     /* the HIP runtime reported a launch error */
+} pisa_status_t;
+
+typedef enum { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype_t;
+
+/* Problem shape. Supported: D in {64, 128}, block in {64, 128}, L >= 1,
+ * B*H >= 1, dtype PISA_F32 or PISA_BF16 (I/O dtype; accumulation is fp32,
+ * block statistics and routing scores are fp64). */
+typedef struct {
+  int32_t B, H, L, D, block;
+  int32_t dtype; /* pisa_dtype_t */
+} pisa_shape_t;
+
+#define PISA_SINK_NONE INT32_MIN /* sink_idx values: PISA_SINK_NONE, 0, -1 */
+
+/* Block statistics (gist summary, "Hardware Implementation", pre-computation
+ * step; symbols of "Core Algorithm"). All pointers are caller-owned device
+ * buffers of the sizes given; n = ceil(L / block).
+ *   qbar  [B,H,n,D] fp64  mean of the query rows of block i
+ *   kbar  [B,H,n,D] fp64  key centroid k̄_j (mean of the block's keys)
+ *   vsum  [B,H,n,D] fp64  ΣV_j, the sum (not mean) of the block's values
+ *   hbar  [B,H,D,D] fp64  H̄[d][e] = (1/n) Σ_j Σ_n (k_n - k̄_j)[d] v_n[e]
+ *   mnorm [B,H,n]   fp64  M_j = ||H_j - H̄||_F; may be NULL unless the
+ *                         covariance-aware routing of pisa_select is used
+ *   ws / ws_bytes         workspace of at least pisa_workspace_bytes(shape)
+ *                         bytes, 256-byte aligned. pisa_block_stats writes
+ *                         operand-ordered copies of K, V, k̄, ΣV and H̄ in the
+ *                         I/O dtype there, which pisa_attn_fwd reads; its
+ *                         content is otherwise unspecified. */
+typedef struct {
+  double *qbar, *kbar, *vsum, *hbar, *mnorm;
+  void *ws;
+  size_t ws_bytes;
+} pisa_stats_t;
+
+/* Bytes of workspace the stats / select / forward calls need for `shape`
+ * (0 if the shape is invalid). */
+size_t pisa_workspace_bytes(const pisa_shape_t *shape);
+
+/* Step 1: block statistics. Reads q, k, v once; writes qbar, kbar, vsum,
+ * hbar (and mnorm when non-NULL) plus the workspace copies. */
+pisa_status_t pisa_block_stats(const pisa_shape_t *shape, const void *q, const void *k,
+                               const void *v, const pisa_stats_t *st, void *stream);
+
+/* Step 2: per-query-block top-k routing (gist summary, "Covariance-Aware
+ * Routing"; README, "Attention sink for MMDiT"). Score of key block j for
+ * query block i: S_ij = scale * q̄_i·k̄_j + cov_weight * M_j (fp64), and
+ * +infinity for the sink block (sink_idx 0: block 0; -1: block n-1;
+ * PISA_SINK_NONE: none). The topk largest scores win; equal scores go to the
+ * lower block index. idx [B,H,n,topk] int32 (device, caller-owned) receives
+ * each query block's selection in ascending order.
+ * Requires: 1 <= topk <= n; cov_weight >= 0 and finite; st->mnorm non-NULL
+ * (computed by pisa_block_stats) when cov_weight > 0; the workspace of
+ * pisa_block_stats (routing scores are staged there). */
+pisa_status_t pisa_select(const pisa_shape_t *shape, const pisa_stats_t *st, double scale,
+                          double cov_weight, int32_t topk, int32_t sink_idx, int32_t *idx,
+                          void *stream);
+
+/* Step 3: fused exact + Taylor online-softmax pass (gist summary, "Core
+ * Algorithm" N_t equation and "Hardware Implementation" phases 1-3).
+ * first_order = 1: hybrid variant (zeroth order plus global first-order
+ * correction, the paper version); 0: zeroth-order-only variant (README,
+ * "Kernel variants"). idx [B,H,n,topk] int32, each row ascending without
+ * repeats, entries in [0, n) (any selection is accepted, e.g. one computed
+ * elsewhere). Keys and values are read from the workspace copies written by
+ * pisa_block_stats for the same q, k, v. o [B,H,L,D] receives the output in
+ * the I/O dtype (round to nearest even). */
+pisa_status_t pisa_attn_fwd(const pisa_shape_t *shape, const void *q, const pisa_stats_t *st,
+                            int32_t first_order, const int32_t *idx, int32_t topk, double scale,
+                            void *o, void *stream);
+
+/* Same-device dense baseline: o = softmax(scale * Q Kᵀ) V per (batch, head)
+ * (the skill page's compute_exact_attention, used as the definition of dense
+ * attention), computed by the same tile loop as pisa_attn_fwd's exact phase
+ * over every key block. ws: at least dense_workspace_bytes(shape) bytes,
+ * 256-byte aligned (operand-ordered K and V copies). */
+size_t dense_workspace_bytes(const pisa_shape_t *shape);
+pisa_status_t dense_attn_fwd(const pisa_shape_t *shape, const void *q, const void *k,
+                             const void *v, double scale, void *o, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/* Human-readable text of a status code (static storage). */
+const char *pisa_status_string(pisa_status_t status);
+
+/* Text of the last HIP error seen by a call on this host thread ("" if none). */
+const char *pisa_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* PISA_H_ */

@@ -1,0 +1,116 @@
+"""The C ABI library loads, exports every declared symbol, and rejects bad
+arguments on the host before anything reaches a GPU (no compute calls here)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_sparse_attention_stats_amd as bsa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pisa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(bsa.LIB_PATH), reason="libpisa.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pisa_\w+|dense_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = bsa.load_library()
+    names = declared_functions()
+    assert set(names) == set(bsa.EXPORTS)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def shape(B=1, H=2, L=1000, D=128, block=64, dtype=bsa.PISA_BF16):
+    return bsa.Shape(B, H, L, D, block, dtype)
+
+
+def test_workspace_sizes():
+    lib = bsa.load_library()
+    s = shape()
+    total = lib.pisa_workspace_bytes(ctypes.byref(s))
+    dense = lib.dense_workspace_bytes(ctypes.byref(s))
+    n = 16
+    kv = 2 * 2 * n * 64 * 128 * 2  # K and V copies of 2 heads
+    assert dense >= kv and dense < kv + 1024
+    assert total >= dense + 2 * n * n * 8  # scores of two heads
+    assert total % 256 == 0 and dense % 256 == 0
+    assert lib.pisa_workspace_bytes(ctypes.byref(shape(D=96))) == 0
+    assert lib.pisa_workspace_bytes(ctypes.byref(shape(block=32))) == 0
+    assert lib.pisa_workspace_bytes(ctypes.byref(shape(L=0))) == 0
+    assert lib.pisa_workspace_bytes(ctypes.byref(shape(dtype=7))) == 0
+    assert lib.pisa_workspace_bytes(None) == 0
+
+
+def test_status_strings():
+    lib = bsa.load_library()
+    for code in range(4):
+        assert lib.pisa_status_string(code).decode()
+    assert lib.pisa_last_hip_error().decode() == ""
+
+
+FAKE = 0x10000  # aligned non-null host address: never dereferenced, validation fails first
+
+
+def stats_struct(ws_bytes=1 << 40, mnorm=FAKE):
+    return bsa.StatsStruct(FAKE, FAKE, FAKE, FAKE, mnorm, FAKE, ws_bytes)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(D=96), bsa.PISA_ENOTSUP), (dict(block=256), bsa.PISA_ENOTSUP),
+    (dict(L=0), bsa.PISA_EINVAL), (dict(B=0), bsa.PISA_EINVAL), (dict(dtype=5), bsa.PISA_EINVAL),
+    (dict(L=64 * 8193), bsa.PISA_ENOTSUP),
+])
+def test_bad_shapes_rejected(kw, code):
+    lib = bsa.load_library()
+    s = shape(**kw)
+    st = stats_struct()
+    assert lib.pisa_block_stats(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.byref(st), None) == code
+    assert lib.pisa_select(ctypes.byref(s), ctypes.byref(st), 0.1, 0.0, 1, bsa.PISA_SINK_NONE, FAKE, None) == code
+    assert lib.pisa_attn_fwd(ctypes.byref(s), FAKE, ctypes.byref(st), 1, FAKE, 1, 0.1, FAKE, None) == code
+    assert lib.dense_attn_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, 1 << 40, None) == code
+
+
+def test_bad_arguments_rejected():
+    lib = bsa.load_library()
+    s = shape()  # n = 16
+    st = stats_struct()
+    E = bsa.PISA_EINVAL
+    sel = lambda st=st, scale=0.1, cw=0.0, k=2, sink=bsa.PISA_SINK_NONE, idx=FAKE: lib.pisa_select(
+        ctypes.byref(s), ctypes.byref(st), scale, cw, k, sink, idx, None)
+    assert sel(k=0) == E and sel(k=17) == E
+    assert sel(sink=1) == E and sel(sink=-2) == E
+    assert sel(cw=-1.0) == E and sel(cw=float("nan")) == E and sel(cw=float("inf")) == E
+    assert sel(scale=0.0) == E and sel(scale=float("nan")) == E
+    assert sel(idx=None) == E and sel(idx=FAKE + 2) == E
+    assert sel(st=stats_struct(mnorm=None), cw=0.5) == E  # covariance routing needs M_j
+    assert sel(st=stats_struct(ws_bytes=10)) == E  # workspace too small
+    st_mis = bsa.StatsStruct(FAKE + 4, FAKE, FAKE, FAKE, None, FAKE, 1 << 40)
+    assert sel(st=st_mis) == E  # misaligned fp64 buffer
+    st_ws = bsa.StatsStruct(FAKE, FAKE, FAKE, FAKE, None, FAKE + 16, 1 << 40)
+    assert sel(st=st_ws) == E  # workspace not 256-aligned
+    fwd = lambda q=FAKE, o=FAKE, fo=1, idx=FAKE, k=2, scale=0.1: lib.pisa_attn_fwd(
+        ctypes.byref(s), q, ctypes.byref(st), fo, idx, k, scale, o, None)
+    assert fwd(q=None) == E and fwd(q=FAKE + 8) == E and fwd(o=None) == E
+    assert fwd(fo=2) == E and fwd(k=0) == E and fwd(k=17) == E and fwd(idx=None) == E
+    assert fwd(scale=-1.0) == E
+    assert lib.pisa_block_stats(ctypes.byref(s), FAKE, None, FAKE, ctypes.byref(st), None) == E
+    assert lib.pisa_block_stats(ctypes.byref(s), FAKE, FAKE, FAKE, None, None) == E
+    assert lib.dense_attn_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, 10, None) == E
+    assert lib.dense_attn_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, 0.1, FAKE, FAKE + 1, 1 << 40, None) == E
+    assert lib.pisa_last_hip_error().decode() == ""
+
+
+def test_topk_rule_matches_table():
+    cases = {(0.25, 16): 4, (0.15, 72): 10, (0.125, 1182): 147, (0.10, 1861): 186,
+             (0.05, 591): 29, (1.0, 591): 591, (0.0, 5): 1}
+    for (d, n), k in cases.items():
+        assert bsa.topk_from_density(d, n) == k

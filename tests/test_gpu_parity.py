@@ -1,0 +1,164 @@
+"""GPU parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Small shapes are compared in full (every head, every query block); the
+full-size DiT-shaped workloads run on all heads in the same launch
+configuration as the bench and are compared on sampled heads and query blocks
+that the oracle evaluates one by one.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_attention_stats_amd as bsa
+import oracle
+import synth
+from parity import check_workload, compare_out, log, sample_qblocks
+
+pytestmark = pytest.mark.gpu
+
+W = synth.Workload
+
+SMALL = [
+    # tiles spanning several sub-tiles, ragged tails, both block sizes, both dtypes
+    W("small_bf16_ragged", 1, 3, 1000, 128, 64, 0.25, "bf16", "hyd", None, 0.0, seed=11),
+    W("small_bf16_0th", 2, 2, 777, 128, 64, 0.2, "bf16", "0th", None, 0.0, seed=12),
+    W("small_bf16_blk128", 1, 2, 1100, 128, 128, 0.3, "bf16", "hyd", None, 0.0, seed=13),
+    W("small_bf16_blk128_short_last", 1, 2, 1050, 128, 128, 0.3, "bf16", "0th", -1, 0.0, seed=14),
+    W("small_bf16_d64", 1, 2, 900, 64, 64, 0.25, "bf16", "hyd", 0, 0.0, seed=15),
+    W("small_f32_d128", 1, 2, 700, 128, 64, 0.3, "f32", "hyd", -1, 0.0, seed=16),
+    W("small_f32_blk128", 1, 1, 800, 64, 128, 0.5, "f32", "hyd", None, 0.0, seed=17),
+    W("small_bf16_cov", 1, 2, 1200, 128, 64, 0.15, "bf16", "hyd", 0, 0.1, seed=18),
+    W("small_bf16_cov_balanced", 1, 2, 1200, 128, 64, 0.15, "bf16", "hyd", None, 1e-3, seed=19),
+    W("small_f32_cov", 1, 2, 640, 64, 64, 0.2, "f32", "0th", None, 0.05, seed=20),
+]
+
+EDGES = [
+    W("edge_single_block", 1, 2, 40, 128, 64, 0.5, "bf16", "hyd", None, 0.0, seed=21),
+    W("edge_one_token", 1, 1, 1, 64, 64, 1.0, "f32", "hyd", -1, 0.0, seed=22),
+    W("edge_last_block_one_token", 1, 2, 65, 128, 64, 0.5, "bf16", "hyd", -1, 0.0, seed=23),
+    W("edge_topk_one", 1, 2, 640, 128, 64, 0.01, "bf16", "hyd", None, 0.0, seed=24),
+    W("edge_topk_one_sink_last", 1, 2, 650, 128, 64, 0.01, "bf16", "hyd", -1, 0.0, seed=25),
+    W("edge_density_one", 1, 2, 600, 128, 64, 1.0, "bf16", "hyd", None, 0.0, seed=26),
+    W("edge_density_one_f32", 1, 2, 333, 64, 128, 1.0, "f32", "0th", None, 0.0, seed=27),
+    W("edge_topk_n_minus_1", 1, 2, 500, 128, 64, 0.99, "bf16", "hyd", 0, 0.0, seed=28),
+]
+
+
+@pytest.fixture(autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_small_full_parity(w):
+    check_workload(w)
+
+
+@pytest.mark.parametrize("w", EDGES, ids=lambda w: w.name)
+def test_edge_cases(w):
+    check_workload(w)
+
+
+def test_tiny_config_full():
+    check_workload(synth.TINY)
+
+
+def test_flux_config_full():
+    check_workload(synth.FLUX)
+
+
+def test_wan_config_sampled():
+    w = synth.WAN
+    check_workload(w, heads=[(0, 0), (0, 17), (0, 39)], qblock_sample=10)
+
+
+def test_hunyuan_config_sampled():
+    w = synth.HUNYUAN
+    check_workload(w, heads=[(0, 0), (0, 23)], qblock_sample=10)
+
+
+@pytest.mark.parametrize("w", synth.sweep(), ids=lambda w: w.name)
+def test_sweep_points_reduced_length(w):
+    """Every block x density x variant point of the sweep at L = 9450 (an
+    eighth of the Wan length, same ragged tail structure), both batch rows."""
+    check_workload(w.replace(L=9450, H=2), qblock_sample=None)
+
+
+@pytest.mark.parametrize("blk,density,variant", [(128, 0.05, "hyd"), (64, 0.5, "0th")])
+def test_sweep_full_size_sampled(blk, density, variant):
+    w = synth.SWEEP_BASE.replace(block=blk, density=density, variant=variant,
+                                 name=f"sweep_full_b{blk}_d{density}_{variant}")
+    check_workload(w, heads=[(1, 5)], qblock_sample=6)
+
+
+def test_dense_baseline_parity():
+    dev = torch.device("cuda:0")
+    for w in (W("dense_bf16", 1, 2, 1000, 128, 64, 1.0, "bf16", seed=31),
+              W("dense_f32", 1, 1, 777, 64, 64, 1.0, "f32", seed=32)):
+        q, k, v = synth.make_qkv(w)
+        o = bsa.dense(*(x.to(dev) for x in (q, k, v))).float().cpu().numpy()
+        for h in range(w.H):
+            ref = oracle.dense_rows(*(synth.as_f64(x[0, h]) for x in (q, k, v)), slice(0, w.L), w.scale)
+            compare_out(o[0, h], ref, w.dtype, f"{w.name} head {h}")
+
+
+def test_dense_baseline_wan_shape_sampled():
+    w = synth.WAN.replace(H=2)
+    dev = torch.device("cuda:0")
+    q, k, v = synth.make_qkv(w)
+    o = bsa.dense(*(x.to(dev) for x in (q, k, v))).float().cpu().numpy()
+    for h in range(2):
+        qh, kh, vh = (synth.as_f64(x[0, h]) for x in (q, k, v))
+        for i in sample_qblocks(w.n_blocks, 4, 3):
+            r = slice(i * 64, min(w.L, (i + 1) * 64))
+            ref = oracle.dense_rows(qh, kh, vh, r, w.scale)
+            compare_out(o[0, h, r], ref, w.dtype, f"dense wan head {h} query block {i}")
+
+
+def test_density_one_equals_dense_on_gpu():
+    w = W("d1", 1, 2, 1000, 128, 64, 1.0, "bf16", seed=33)
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in synth.make_qkv(w))
+    o1 = bsa.piecewise_sparse_attention_hyd(q, k, v, density=1.0).float()
+    o2 = bsa.dense(q, k, v).float()
+    assert (o1 - o2).abs().max().item() <= 1e-2
+
+
+def test_constant_values_give_constant_output():
+    """Normalisation consistency at a DiT shape: v_t = c ⇒ o_t = c."""
+    w = synth.FLUX.replace(H=4)
+    dev = torch.device("cuda:0")
+    q, k, _ = synth.make_qkv(w)
+    c = torch.linspace(-2, 2, w.D, dtype=torch.float32).to(torch.bfloat16)
+    v = c.expand(w.B, w.H, w.L, w.D).contiguous()
+    for fn in (bsa.piecewise_sparse_attention_hyd, bsa.piecewise_sparse_attention_0th):
+        o = fn(q.to(dev), k.to(dev), v.to(dev), density=w.density, sink_idx=0).float().cpu()
+        assert (o - c.float()).abs().max().item() <= 2e-2
+
+
+def test_deterministic_and_stream_ordered():
+    w = synth.FLUX.replace(H=3)
+    dev = torch.device("cuda:0")
+    q, k, v = (x.to(dev) for x in synth.make_qkv(w))
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        o1, i1 = bsa.piecewise_sparse_attention_hyd(q, k, v, density=0.15, return_idx=True)
+    s.synchronize()
+    o2, i2 = bsa.piecewise_sparse_attention_hyd(q, k, v, density=0.15, return_idx=True)
+    torch.cuda.synchronize()
+    assert torch.equal(i1, i2)
+    assert torch.equal(o1, o2)
+
+
+def test_bad_arguments_raise_before_launch():
+    dev = torch.device("cuda:0")
+    q = torch.zeros(1, 1, 100, 96, dtype=torch.bfloat16, device=dev)
+    with pytest.raises(bsa.PisaError):
+        bsa.piecewise_sparse_attention_hyd(q, q, q, density=0.5)
+    q = torch.zeros(1, 1, 100, 128, dtype=torch.bfloat16, device=dev)
+    st = bsa.block_stats(q, q, q)
+    with pytest.raises(bsa.PisaError):
+        bsa.select(st, topk=3, scale=0.1)  # n = 2
+    torch.cuda.synchronize()
