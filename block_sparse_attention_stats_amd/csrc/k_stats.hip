@@ -76,6 +76,7 @@ __global__ __launch_bounds__(256) void k_block_stats(StatsArgs a) {
   }
 
   double csum[2] = {0.0, 0.0};  // column-sum tasks p = tid, tid + 256 over (tensor, d)
+  float kn2max = 0.0f;          // largest squared key norm seen by this thread's rows
 
   uint4 pre[NT][PER];
   auto load_sub = [&](int s) {
@@ -128,6 +129,20 @@ __global__ __launch_bounds__(256) void k_block_stats(StatsArgs a) {
           csum[u] += sacc;
         }
       }
+    }
+
+    // ---- squared key norms (bound of the logits used by the fused pass)
+    if constexpr (kDoPack) {
+      const int row = tid >> 2, part = tid & 3;
+      float ss = 0.0f;
+#pragma unroll 8
+      for (int d = part * (D / 4); d < (part + 1) * (D / 4); ++d) {
+        const float x = O::to_f32(*(const T*)(&tile[KT][row * PITCH + d * ESZ]));
+        ss = fmaf(x, x, ss);
+      }
+      ss += __shfl_xor(ss, 1);
+      ss += __shfl_xor(ss, 2);
+      kn2max = fmaxf(kn2max, ss);
     }
 
     // ---- operand-ordered copies of K and V
@@ -240,6 +255,15 @@ __global__ __launch_bounds__(256) void k_block_stats(StatsArgs a) {
     }
   }
 
+  if constexpr (kDoPack) {
+    __shared__ float kred[4];
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) kn2max = fmaxf(kn2max, __shfl_xor(kn2max, o));
+    if (lane == 0) kred[wv] = kn2max;
+    __syncthreads();
+    if (tid == 0)
+      a.kmax2[(size_t)bh * a.nch + ch] = fmaxf(fmaxf(kred[0], kred[1]), fmaxf(kred[2], kred[3]));
+  }
   if constexpr (MODE == kStatsFull) {
     float* dst = a.hpart + ((size_t)bh * a.nch + ch) * D * D;
 #pragma unroll

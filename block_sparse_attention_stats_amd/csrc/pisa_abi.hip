@@ -43,6 +43,10 @@ pisa_status_t check_shape(const pisa_shape_t* s, pisa::WsLayout* w) {
   off = align256(off + (size_t)bh * n * w->spb * sub);
   w->vp = off;
   off = align256(off + (size_t)bh * n * w->spb * sub);
+  w->kmax2 = off;
+  off = align256(off + (size_t)bh * w->nch * sizeof(float));
+  w->redo = off;
+  off = align256(off + ((size_t)bh * n * w->spb + 1) * sizeof(int32_t));
   w->dense_total = off;
   w->kbp = off;
   off = align256(off + (size_t)bh * w->nct * sub);
@@ -96,6 +100,7 @@ pisa::StatsArgs stats_args(const pisa_shape_t* s, const pisa::WsLayout& w, const
   a.vbp = base + w.vbp;
   a.hbt = base + w.hbt;
   a.hpart = (float*)(base + w.hpart);
+  a.kmax2 = (float*)(base + w.kmax2);
   a.L = s->L;
   a.n = w.n;
   a.blk = s->block;
@@ -118,6 +123,9 @@ pisa::FwdArgs fwd_args(const pisa_shape_t* s, const pisa::WsLayout& w, const voi
   a.vbp = base + w.vbp;
   a.hbt = base + w.hbt;
   a.idx = idx;
+  a.kmax2 = (const float*)(base + w.kmax2);
+  a.redo = (int*)(base + w.redo);
+  a.nch = w.nch;
   a.total = w.bh * w.n * w.spb;
   a.per_xcd = (a.total + pisa::kNumXcd - 1) / pisa::kNumXcd;
   a.L = s->L;
@@ -130,6 +138,7 @@ pisa::FwdArgs fwd_args(const pisa_shape_t* s, const pisa::WsLayout& w, const voi
   a.scale = (float)scale;
   a.first_order = first_order;
   a.tail = tail;
+  a.map_mode = 0;  // measured: the per-XCD range mapping (1) gains nothing at the Wan shape
   return a;
 }
 

@@ -14,6 +14,8 @@ struct WsLayout {
   size_t hbt;         // H̄ᵀ operand chunks: [BH][D*D]
   size_t hpart;       // fp32 partial Σ_j H_j per chunk of blocks: [BH][nch][D][D]
   size_t scores;      // fp64 routing scores: [BH][n][n]
+  size_t kmax2;       // fp32 largest squared key norm per run of blocks: [BH][nch]
+  size_t redo;        // int32 count + list of query tiles the careful kernel recomputes
   size_t total;       // bytes needed by stats + select + forward
   size_t dense_total; // bytes needed by the dense baseline (kp + vp)
   int n, spb, nct, cb, nch, esz;
@@ -26,6 +28,7 @@ struct StatsArgs {
   double* hbar;
   uint8_t *kp, *vp, *kbp, *vbp, *hbt;
   float* hpart;
+  float* kmax2;
   int L, n, blk, cb, nch, nct;
 };
 
@@ -47,11 +50,14 @@ struct FwdArgs {
   uint8_t* o;
   const uint8_t *kp, *vp, *kbp, *vbp, *hbt;
   const int32_t* idx;  // nullptr: every key block (dense)
+  const float* kmax2;  // [BH][nch] largest squared key norm per run of blocks
+  int* redo;           // [0]: count, [1..]: query tiles left to the careful kernel
   long total, per_xcd;
-  int L, n, blk, topk, n_last, nct;
+  int L, n, blk, topk, n_last, nct, nch;
   float cs;     // scale * log2(e)
   float scale;
   int first_order, tail;
+  int map_mode;  // 0: consecutive workgroups take consecutive query tiles; 1: one range per XCD
 };
 
 enum StatsMode { kStatsFull = 0, kStatsMnorm = 1, kStatsPackOnly = 2 };
@@ -62,6 +68,7 @@ hipError_t launch_block_stats(int dtype, int D, int mode, const StatsArgs& a, lo
 hipError_t launch_hbar_reduce(int dtype, int D, const StatsArgs& a, long bh, hipStream_t s);
 hipError_t launch_scores(int D, const ScoreArgs& a, long bh, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, long rows, hipStream_t s);
+// Fast pass, then the careful pass over the query tiles the fast pass queued.
 hipError_t launch_fwd(int dtype, int D, const FwdArgs& a, hipStream_t s);
 
 constexpr int kMaxBlocks = 8192;  // routing keeps one score row per workgroup in LDS

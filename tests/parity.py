@@ -85,13 +85,14 @@ def run_gpu(w: synth.Workload, q, k, v, oracle_idx=None):
 
 
 def check_workload(w: synth.Workload, heads=None, qblock_sample: int | None = None,
-                   check_gpu_idx_output: bool = True, seed: int = 0):
+                   check_gpu_idx_output: bool = True, seed: int = 0, qkv=None):
     """Full GPU run on all heads; oracle comparison on `heads` (default: all)
-    and, per head, on `qblock_sample` query blocks (default: all)."""
+    and, per head, on `qblock_sample` query blocks (default: all). `qkv`
+    replaces the generated inputs (CPU tensors of the workload's shape)."""
     t0 = time.time()
     log(f"[{w.name}] B={w.B} H={w.H} L={w.L} D={w.D} blk={w.block} d={w.density} {w.variant} "
         f"sink={w.sink_idx} cov={w.cov_weight} {w.dtype}")
-    q, k, v = synth.make_qkv(w)
+    q, k, v = synth.make_qkv(w) if qkv is None else qkv
     dev = torch.device("cuda:0")
     qd, kd, vd = (x.to(dev) for x in (q, k, v))
     n = w.n_blocks
@@ -140,4 +141,5 @@ def check_workload(w: synth.Workload, heads=None, qblock_sample: int | None = No
                 r2 = np.concatenate([np.arange(i * w.block, min(w.L, (i + 1) * w.block)) for i in same])
                 np.testing.assert_array_equal(o_g[b, h, r2], o_o[b, h, r2])
     log(f"[{w.name}] ok in {time.time() - t0:.1f}s; idx rows differing within ties: {res['differ_rows']}")
+    res["stats"] = st
     return res

@@ -93,6 +93,39 @@ def test_sweep_full_size_sampled(blk, density, variant):
     check_workload(w, heads=[(1, 5)], qblock_sample=6)
 
 
+def redo_count(st, w) -> int:
+    """Query tiles the fast kernel left to the careful (running-max) kernel in
+    the last pisa_attn_fwd call: an int32 counter in the workspace, right after
+    the K/V copies and the per-run key-norm maxima."""
+    a256 = lambda x: (x + 255) // 256 * 256
+    bh, n, spb = w.B * w.H, w.n_blocks, w.block // 64
+    esz = 2 if w.dtype == "bf16" else 4
+    kv = a256(bh * n * spb * 64 * w.D * esz)
+    nch = -(-n // (1024 // w.block))
+    off = 2 * kv + a256(bh * nch * 4)
+    return int(st.ws[off:off + 4].view(torch.int32).item())
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_loose_logit_bound_uses_careful_kernel(dtype):
+    """One huge key orthogonal to every query makes the Cauchy–Schwarz bound of
+    the logits ~10^4 log2 units too high: the fast kernel must hand every query
+    tile to the running-max kernel, and the result must still match."""
+    w = W(f"loose_bound_{dtype}", 1, 2, 700, 128, 64, 0.25, dtype, "hyd", None, 0.0, seed=41)
+    q, k, v = synth.make_qkv(w)
+    q[..., 0] = 0
+    k[:, :, 130, :] = 0
+    k[:, :, 130, 0] = 3.0e4
+    res = check_workload(w, qkv=(q, k, v))
+    assert redo_count(res["stats"], w) == w.B * w.H * w.n_blocks
+
+
+def test_tight_bound_uses_fast_kernel_only():
+    w = synth.FLUX.replace(H=2, L=2000)
+    res = check_workload(w)
+    assert redo_count(res["stats"], w) == 0
+
+
 def test_dense_baseline_parity():
     dev = torch.device("cuda:0")
     for w in (W("dense_bf16", 1, 2, 1000, 128, 64, 1.0, "bf16", seed=31),
