@@ -47,6 +47,8 @@ pisa_status_t check_shape(const pisa_shape_t* s, pisa::WsLayout* w) {
   off = align256(off + (size_t)bh * w->nch * sizeof(float));
   w->redo = off;
   off = align256(off + ((size_t)bh * n * w->spb + 1) * sizeof(int32_t));
+  w->sync = off;
+  off = align256(off + sizeof(int32_t));
   w->dense_total = off;
   w->kbp = off;
   off = align256(off + (size_t)bh * w->nct * sub);
@@ -125,9 +127,10 @@ pisa::FwdArgs fwd_args(const pisa_shape_t* s, const pisa::WsLayout& w, const voi
   a.idx = idx;
   a.kmax2 = (const float*)(base + w.kmax2);
   a.redo = (int*)(base + w.redo);
+  a.sync = (int*)(base + w.sync);
+  a.sync_ticks = 20000;  // 200 us, about one workgroup's lifetime at the Wan shape
   a.nch = w.nch;
   a.total = w.bh * w.n * w.spb;
-  a.per_xcd = (a.total + pisa::kNumXcd - 1) / pisa::kNumXcd;
   a.L = s->L;
   a.n = w.n;
   a.blk = s->block;
@@ -138,7 +141,6 @@ pisa::FwdArgs fwd_args(const pisa_shape_t* s, const pisa::WsLayout& w, const voi
   a.scale = (float)scale;
   a.first_order = first_order;
   a.tail = tail;
-  a.map_mode = 0;  // measured: the per-XCD range mapping (1) gains nothing at the Wan shape
   return a;
 }
 

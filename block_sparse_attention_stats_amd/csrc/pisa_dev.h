@@ -58,6 +58,25 @@ struct Op<bf16> {
   }
   __device__ static inline float to_f32(bf16 x) { return (float)x; }
   __device__ static inline bf16 from_f32(float x) { return (bf16)x; }
+  // acc + the sum of the KW rounded values held in one packed chunk
+  __device__ static inline float rowsum(const uint4& c, float acc) {
+    typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, c.x), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, c.y), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, c.z), one, acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, c.w), one, acc, false);
+    return acc;
+  }
+  // acc + the dot product of two packed chunks (fp32 products and sums)
+  __device__ static inline float dot(const uint4& x, const uint4& y, float acc) {
+    typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.x), __builtin_bit_cast(bf16x2, y.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.y), __builtin_bit_cast(bf16x2, y.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.z), __builtin_bit_cast(bf16x2, y.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x.w), __builtin_bit_cast(bf16x2, y.w), acc, false);
+    return acc;
+  }
 };
 
 template <>
@@ -75,6 +94,14 @@ struct Op<float> {
   }
   __device__ static inline float to_f32(float x) { return x; }
   __device__ static inline float from_f32(float x) { return x; }
+  __device__ static inline float rowsum(const uint4& c, float acc) {
+    const f32x4 v = __builtin_bit_cast(f32x4, c);
+    return acc + ((v[0] + v[1]) + (v[2] + v[3]));
+  }
+  __device__ static inline float dot(const uint4& x, const uint4& y, float acc) {
+    const f32x4 a = __builtin_bit_cast(f32x4, x), b = __builtin_bit_cast(f32x4, y);
+    return fmaf(a[3], b[3], fmaf(a[2], b[2], fmaf(a[1], b[1], fmaf(a[0], b[0], acc))));
+  }
 };
 
 // Geometry of the packed, operand-ordered copies of one (batch, head).
@@ -116,14 +143,6 @@ __host__ __device__ constexpr int vfmt_offset(int kk, int d) {
   const int c = r / G::KW, e = r % G::KW;
   const int dt = d >> 5, lane = h * 32 + (d & 31);
   return ((((w * G::DT + dt) * G::CPK + c) * kWave + lane) * G::KW + e) * G::ESZ;
-}
-
-// Maps a launched workgroup to a logical work item so that each of the XCDs
-// gets one contiguous range of items (one or a few heads), keeping a head's
-// K/V and centroid tiles in that XCD's L2. Returns -1 for padding workgroups.
-__device__ inline long xcd_remap(long p, long total, long per_xcd) {
-  const long logical = (p % kNumXcd) * per_xcd + p / kNumXcd;
-  return logical < total ? logical : -1;
 }
 
 __device__ inline float wave_max(float x) {

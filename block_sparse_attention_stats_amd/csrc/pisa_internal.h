@@ -16,6 +16,7 @@ struct WsLayout {
   size_t scores;      // fp64 routing scores: [BH][n][n]
   size_t kmax2;       // fp32 largest squared key norm per run of blocks: [BH][nch]
   size_t redo;        // int32 count + list of query tiles the careful kernel recomputes
+  size_t sync;        // int32 arrival counter of the fast kernel's generation barrier
   size_t total;       // bytes needed by stats + select + forward
   size_t dense_total; // bytes needed by the dense baseline (kp + vp)
   int n, spb, nct, cb, nch, esz;
@@ -52,12 +53,14 @@ struct FwdArgs {
   const int32_t* idx;  // nullptr: every key block (dense)
   const float* kmax2;  // [BH][nch] largest squared key norm per run of blocks
   int* redo;           // [0]: count, [1..]: query tiles left to the careful kernel
-  long total, per_xcd;
+  int* sync;           // arrival counter of the generation barrier of the fast kernel
+  long nwg;            // resident workgroups of the fast kernel (persistent grid)
+  int sync_ticks;      // longest wait at a generation barrier, in 100 MHz ticks
+  long total;
   int L, n, blk, topk, n_last, nct, nch;
   float cs;     // scale * log2(e)
   float scale;
   int first_order, tail;
-  int map_mode;  // 0: consecutive workgroups take consecutive query tiles; 1: one range per XCD
 };
 
 enum StatsMode { kStatsFull = 0, kStatsMnorm = 1, kStatsPackOnly = 2 };
@@ -72,6 +75,5 @@ hipError_t launch_topk(const TopkArgs& a, long rows, hipStream_t s);
 hipError_t launch_fwd(int dtype, int D, const FwdArgs& a, hipStream_t s);
 
 constexpr int kMaxBlocks = 8192;  // routing keeps one score row per workgroup in LDS
-constexpr int kNumXcd = 8;        // XCDs of an MI355X; workgroups are dealt to them round-robin
 
 }  // namespace pisa
