@@ -28,6 +28,34 @@ METRIC = "PISA attn fwd ms/call + effective TFLOP/s (%MFMA peak), Wan-shape L=75
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}  # MI355X dense MFMA peaks
 HBM_PEAK_GBS = 8000.0
 
+# Bytes one k_pisa_fwd launch moves between L2 and memory at the Wan shape, from
+# two rocprofv3 --pmc passes over this bench command (FETCH_SIZE, then
+# WRITE_SIZE; KiB per dispatch, mean of the two dispatches), each scaled by what
+# the same counter reads for one plain 2 GiB device copy (bench.py --calib-copy 2):
+# FETCH_SIZE reads 1048612 KiB for it (scale 2.0), WRITE_SIZE 2097152 KiB (1.0).
+# The figures hold only for the kernel sources they were taken on; their SHA-1
+# is kept, and the figure is reported as null once the sources differ.
+FUSED_TRAFFIC = {"workload": "wan_bf16",
+                 "sources": ["k_fwd.hip", "pisa_dev.h", "pisa_internal.h", "pisa_abi.hip"],
+                 "sha1": "e53e36019f01192690c1e96fb19ac51614fc79b0",
+                 "fetch_kib": (38118493.5 + 40413602.9375) / 2, "fetch_scale": 2.0,
+                 "write_kib": (757477.5 + 757477.9375) / 2, "write_scale": 1.0}
+
+
+def fused_traffic(workload: str):
+    import hashlib
+
+    t = FUSED_TRAFFIC
+    if workload != t["workload"]:
+        return None
+    h = hashlib.sha1()
+    for f in t["sources"]:
+        with open(os.path.join(ROOT, "block_sparse_attention_stats_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest() != t["sha1"]:
+        return None
+    return 1024.0 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])
+
 
 def flops_from_idx(idx: np.ndarray, L: int, D: int, block: int, first_order: bool) -> dict:
     """Credited FLOPs of one fused call: 4·D per exact (query, key) pair, 4·D
@@ -41,7 +69,7 @@ def flops_from_idx(idx: np.ndarray, L: int, D: int, block: int, first_order: boo
     has_last = (idx == n - 1).any(axis=-1)                      # [B,H,n]
     exact_keys = k * block - (block - n_last) * has_last          # Σ_{j∈S_i} n_j
     exact = float((nq * 4.0 * D * exact_keys).sum())
-    tail = float((nq * 4.0 * D * (n - k)).sum()) * 1.0
+    tail = float((nq * 4.0 * D * (n - k)).sum()) * B * H
     corr = float(2.0 * D * D * nq.sum() * B * H) if (first_order and k < n) else 0.0
     return dict(exact=exact, tail=tail, corr=corr, total=exact + tail + corr)
 
@@ -60,8 +88,9 @@ def stats_bytes(B, H, L, D, block, esz) -> float:
 
 
 def cpu_baseline(w, budget_s: float = 15.0) -> dict:
-    """The fp64 oracle on one head: statistics and routing of the whole head,
-    then query blocks one by one until the time budget is spent."""
+    """The fp64 oracle, whole heads at a time (statistics, routing and every
+    query block of the head), until the time budget is spent; at least one
+    head. Credited with the same FLOPs as the GPU pass over those heads."""
     import oracle
     import synth
 
@@ -70,36 +99,30 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
     except Exception:
         threads = 1
-    q, k, v = (synth.as_f64(x) for x in synth.head_tensors(w, 0, 0))
     n = w.n_blocks
     topk = oracle.topk_from_density(w.density, n)
-    t0 = time.perf_counter()
-    st = oracle.block_stats(q, k, v, w.block)
-    M = oracle.cov_norm(st["H"], st["Hbar"]) if w.cov_weight else None
-    S = oracle.pooled_scores(st["qbar"], st["kbar"], w.scale, M, w.cov_weight, w.sink_idx)
-    idx = oracle.select_topk(S, topk)
-    t_pre = time.perf_counter() - t0
-    order = np.random.default_rng(0).permutation(n)
-    done = []
-    t1 = time.perf_counter()
-    for i in order:
-        oracle.pisa_rows(q, k, v, st, idx[i], int(i), w.block, w.scale, w.variant == "hyd")
-        done.append(int(i))
-        if time.perf_counter() - t1 > budget_s:
-            break
-    t_rows = time.perf_counter() - t1
     sizes = oracle.block_sizes(w.L, w.block).astype(np.float64)
-    total = 0.0
-    for i in done:
-        total += sizes[i] * (4.0 * w.D * sizes[idx[i]].sum() + 4.0 * w.D * (n - topk))
-        if w.variant == "hyd" and topk < n:
-            total += 2.0 * sizes[i] * w.D * w.D
-    share = len(done) / n
-    t = t_rows + t_pre * share
+    total, t, heads = 0.0, 0.0, []
+    for (b, h) in [(b, h) for b in range(w.B) for h in range(w.H)]:
+        q, k, v = (synth.as_f64(x) for x in synth.head_tensors(w, b, h))
+        t0 = time.perf_counter()
+        st = oracle.block_stats(q, k, v, w.block)
+        M = oracle.cov_norm(st["H"], st["Hbar"]) if w.cov_weight else None
+        S = oracle.pooled_scores(st["qbar"], st["kbar"], w.scale, M, w.cov_weight, w.sink_idx)
+        idx = oracle.select_topk(S, topk)
+        for i in range(n):
+            oracle.pisa_rows(q, k, v, st, idx[i], i, w.block, w.scale, w.variant == "hyd")
+        t += time.perf_counter() - t0
+        heads.append((b, h))
+        for i in range(n):
+            total += sizes[i] * (4.0 * w.D * sizes[idx[i]].sum() + 4.0 * w.D * (n - topk))
+            if w.variant == "hyd" and topk < n:
+                total += 2.0 * sizes[i] * w.D * w.D
+        if t > budget_s:
+            break
     return {"value": total / t / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"head (0,0) of {w.name}: statistics + routing of the whole head "
-                      f"({t_pre:.2f}s, charged pro rata), then {len(done)} of {n} query blocks "
-                      f"({t_rows:.1f}s), fp64 NumPy",
+            "sample": f"{len(heads)} whole heads of {w.name} (statistics, routing and all {n} query "
+                      f"blocks each) in {t:.1f}s, fp64 NumPy; input generation not timed",
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
@@ -113,6 +136,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--calib-copy", type=float, default=0.0, metavar="GIB",
+                    help="only run one plain device-to-device copy of GIB GiB and exit: the "
+                         "known-size kernel that scales the HBM byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the path shards over "
@@ -124,8 +150,17 @@ def main():
     import block_sparse_attention_stats_amd as bsa
     import synth
 
-    w = synth.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
+    if args.calib_copy > 0:
+        nbytes = int(args.calib_copy * 2**30)
+        src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calib_copy_bytes": nbytes}), flush=True)
+        return
+
+    w = synth.WORKLOADS[args.workload]
     t0 = time.time()
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     q, k, v = synth.make_qkv(w)
@@ -230,7 +265,8 @@ def main():
         "stats_gbs": sbytes / (ms["block_stats"] * 1e-3) / 1e9,
         "stats_hbm_frac": sbytes / (ms["block_stats"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
         "roofline": {"kernel": "k_pisa_fwd", "bound": "mfma", "achieved": fused_tflops, "peak": peak,
-                     "unit": "TFLOP/s", "frac": fused_tflops / peak, "traffic": None},
+                     "unit": "TFLOP/s", "frac": fused_tflops / peak,
+                     "traffic": fused_traffic(w.name), "traffic_unit": "bytes per launch"},
         "dense": dense,
         "cpu_baseline": cpu,
     }

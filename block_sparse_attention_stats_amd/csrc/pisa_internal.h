@@ -54,7 +54,7 @@ struct FwdArgs {
   const float* kmax2;  // [BH][nch] largest squared key norm per run of blocks
   int* redo;           // [0]: count, [1..]: query tiles left to the careful kernel
   int* sync;           // arrival counter of the generation barrier of the fast kernel
-  long nwg;            // resident workgroups of the fast kernel (persistent grid)
+  long nwg;            // workgroups per generation of the fast kernel (as many as are resident)
   int sync_ticks;      // longest wait at a generation barrier, in 100 MHz ticks
   long total;
   int L, n, blk, topk, n_last, nct, nch;
