@@ -209,6 +209,77 @@ __device__ __forceinline__ void interleave_tile() {
   }
 }
 
+// One software-pipelined sub-tile for bf16 operands, in an explicit order: the
+// MFMAs of PV(t) (Oᵀ += Vᵀ P(t)) and then of Sᵀ(t+2) (accumulated onto `init`)
+// alternate one by one with the weights of tile t+1 (P(t+1) = 2^(Sᵀ(t+1)·cs − m),
+// rounded and packed in pairs, each pair's sum added to acc). A V or K register
+// chunk is reloaded for two tiles ahead right after the last MFMA that reads it.
+// sched_barrier pins the order: with one wavefront per SIMD, the MFMA pipe and
+// the VALU only overlap where the instruction stream alternates, and the
+// compiler's own schedule of this block leaves long runs of either kind.
+// One accumulator element into a VGPR, read where it is needed rather than as
+// part of a copy of the whole accumulator.
+__device__ __forceinline__ float acc_read(float x) {
+  float y;
+  asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(y) : "a"(x));
+  return y;
+}
+
+template <int D>
+__device__ __forceinline__ void xstep(typename Regs<bf16, D>::Acc& oacc,
+                                      typename Regs<bf16, D>::V& vc,
+                                      const typename Regs<bf16, D>::P& pc,
+                                      typename Regs<bf16, D>::K& kc,
+                                      const typename Regs<bf16, D>::Q& qr, f32x16 (&sx)[2],
+                                      const f32x16& init, const f32x16 (&sy)[2],
+                                      typename Regs<bf16, D>::P& py, float (&acc)[2],
+                                      const float (&m)[2], float cs, const uint8_t* vnext,
+                                      const uint8_t* knext, int w, int lane) {
+  using G = Geo<bf16, D>;
+  typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  constexpr int NV = G::DT * G::CPK;
+  constexpr int NPV = 2 * NV, NM = NPV + 2 * G::NC;
+  constexpr int EPM = 32 / NM;  // weights formed per MFMA
+  static_assert(NM * EPM == 32, "32 weights per lane and sub-tile");
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  uint32_t pw[2][4 * G::CPK];
+  float pend = 0.f;
+  sx[0] = init;
+  sx[1] = init;
+#pragma unroll
+  for (int mi = 0; mi < NM; ++mi) {
+    if (mi < NPV) {
+      const int x = mi >> 1, qt = mi & 1;
+      Op<bf16>::mma(oacc[x / G::CPK][qt], vc[x], pc[qt][x % G::CPK]);
+      if (qt == 1 && vnext != nullptr)
+        vc[x] = *(const uint4*)(vnext + ((w * NV + x) * kWave + lane) * 16);
+    } else {
+      const int c = (mi - NPV) >> 1, qt = (mi - NPV) & 1;
+      Op<bf16>::mma(sx[qt], kc[c], qr[qt][c]);
+      if (qt == 1 && knext != nullptr)
+        kc[c] = *(const uint4*)(knext + ((w * G::NC + c) * kWave + lane) * 16);
+    }
+#pragma unroll
+    for (int u = 0; u < EPM; ++u) {
+      const int e = mi * EPM + u, qt = e >> 4, r = e & 15;
+      const float p = __builtin_amdgcn_exp2f(fmaf(acc_read(sy[qt][r]), cs, -m[qt]));
+      if (r & 1) {
+        const bf16x2 pr = {(bf16)pend, (bf16)p};
+        acc[qt] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc[qt], false);
+        pw[qt][r >> 1] = __builtin_bit_cast(uint32_t, pr);
+      } else {
+        pend = p;
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int c = 0; c < G::CPK; ++c)
+      py[qt][c] = make_uint4(pw[qt][4 * c], pw[qt][4 * c + 1], pw[qt][4 * c + 2], pw[qt][4 * c + 3]);
+}
+
 // Careful kernel only: does any row of this sub-tile need a higher running max?
 template <int KIND>
 __device__ __forceinline__ bool tile_max(const f32x16 (&sacc)[2], const float (&m)[2],
@@ -273,12 +344,16 @@ __device__ __forceinline__ void step(typename Regs<T, D>::Acc& oacc, const typen
 // forms P(t+1) from Sᵀ(t+1). K and V are double-buffered in registers: the
 // loads of V(t+2) and K(t+4) are issued during tile t, two tiles before use,
 // which hides the latency of gathers that miss the L2.
-template <typename T, int D, typename Off, typename Init, typename Wts>
+template <typename T, int D, typename Off, typename Init>
 __device__ __forceinline__ void pipelined(int nt, const uint8_t* kbase, const uint8_t* vbase,
-                                          const Off& off, const Init& init, const Wts& wts,
+                                          const Off& off, const Init& init, float (&acc)[2],
+                                          const float (&m)[2], float cs,
                                           const typename Regs<T, D>::Q& qr,
                                           typename Regs<T, D>::Acc& oacc, int w, int lane) {
   if (nt <= 0) return;
+  auto wts = [&](const f32x16 (&sx)[2], typename Regs<T, D>::P& px) {
+    weights_full<T, D>(sx, m, acc, px, cs);
+  };
   typename Regs<T, D>::K kc0, kc1;
   typename Regs<T, D>::V vc0, vc1;
   f32x16 sa[2], sb[2];
@@ -288,35 +363,43 @@ __device__ __forceinline__ void pipelined(int nt, const uint8_t* kbase, const ui
   auto sm = [&](const typename Regs<T, D>::K& kc, f32x16 (&sx)[2], int t) {
     mma_s<T, D>(qr, kc, sx, init(t));
   };
+  // The prologue has no conditions (tiles past the end are replaced by the
+  // last one, and Sᵀ(1) of a one-tile run is never used), so that every path
+  // into the loop has issued the same loads in the same order: the waits the
+  // compiler places in the loop then only cover the tile about to be used.
+  const int tl = nt - 1;
   ldk(kc0, 0);
   ldv(vc0, 0);
-  if (nt > 1) {
-    ldk(kc1, 1);
-    ldv(vc1, 1);
-  }
+  ldk(kc1, min(1, tl));
+  ldv(vc1, min(1, tl));
   sm(kc0, sa, 0);
-  if (nt > 2) ldk(kc0, 2);
+  ldk(kc0, min(2, tl));
   wts(sa, pa);
-  if (nt > 1) {
-    sm(kc1, sb, 1);
-    if (nt > 3) ldk(kc1, 3);
-  }
+  sm(kc1, sb, 1);
+  ldk(kc1, min(3, tl));
   int t = 0;
   // invariant at the top: pa = P(t), sb = S(t+1), kc0 = K(t+2), kc1 = K(t+3),
   // vc0 = V(t), vc1 = V(t+1) (each where the tile exists)
   for (; t + 5 < nt; t += 2) {
-    mma_pv<T, D>(oacc, vc0, pa);  // PV(t)
-    ldv(vc0, t + 2);
-    sm(kc0, sa, t + 2);           // S(t+2)
-    ldk(kc0, t + 4);
-    wts(sb, pb);                  // P(t+1)
-    interleave_tile();
-    mma_pv<T, D>(oacc, vc1, pb);  // PV(t+1)
-    ldv(vc1, t + 3);
-    sm(kc1, sb, t + 3);           // S(t+3)
-    ldk(kc1, t + 5);
-    wts(sa, pa);                  // P(t+2)
-    interleave_tile();
+    if constexpr (sizeof(T) == 2) {
+      xstep<D>(oacc, vc0, pa, kc0, qr, sa, init(t + 2), sb, pb, acc, m, cs, vbase + off(t + 2),
+               kbase + off(t + 4), w, lane);  // PV(t), S(t+2), P(t+1)
+      xstep<D>(oacc, vc1, pb, kc1, qr, sb, init(t + 3), sa, pa, acc, m, cs, vbase + off(t + 3),
+               kbase + off(t + 5), w, lane);  // PV(t+1), S(t+3), P(t+2)
+    } else {
+      mma_pv<T, D>(oacc, vc0, pa);  // PV(t)
+      ldv(vc0, t + 2);
+      sm(kc0, sa, t + 2);           // S(t+2)
+      ldk(kc0, t + 4);
+      wts(sb, pb);                  // P(t+1)
+      interleave_tile();
+      mma_pv<T, D>(oacc, vc1, pb);  // PV(t+1)
+      ldv(vc1, t + 3);
+      sm(kc1, sb, t + 3);           // S(t+3)
+      ldk(kc1, t + 5);
+      wts(sa, pa);                  // P(t+2)
+      interleave_tile();
+    }
   }
   // 1 to 5 tiles left
   const int r = nt - t;
@@ -473,7 +556,8 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
                                            typename Regs<T, D>::Xo& xo) {
   using G = Geo<T, D>;
   constexpr int NC = G::NC, DT = G::DT, ESZ = G::ESZ, KW = G::KW;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, h = lane >> 5, l32 = lane & 31;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
   constexpr int spb = SPB;
   const int half = (int)(item % spb);
   const long rest = item / spb;
@@ -484,7 +568,12 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
 
   constexpr bool dense = DENSE;
   const int nsel = dense ? a.n : a.topk;
-  const int32_t* myidx = dense ? nullptr : a.idx + (bh * a.n + i) * (long)a.topk;
+  // The selection is read-only during the launch. Reading it through the
+  // constant address space makes its (uniform) loads scalar loads, which are
+  // counted apart from the vector loads: taking the next block index never waits
+  // for the K/V gathers already in flight.
+  using cidx_t = const int32_t __attribute__((address_space(4)));
+  const cidx_t* myidx = dense ? nullptr : (const cidx_t*)(a.idx + (bh * a.n + i) * (long)a.topk);
   const bool tail = a.tail && !dense && nsel < a.n;
   // indices outside [0, n) are clamped: a bad selection cannot read out of bounds
   auto block_at = [&](int s) { return dense ? s : min(max(myidx[s], 0), a.n - 1); };
@@ -558,7 +647,7 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
     };
     pipelined<T, D>(
         nt, a.kp, a.vp, off, [](int) { return f32x16{}; },
-        [&](const f32x16 (&sx)[2], typename Regs<T, D>::P& px) { weights_full<T, D>(sx, m, l, px, cs); },
+        l, m, cs,
         qr, oacc, w, lane);
     if (ragged_last) {
       // the short last block: keys beyond n_last start at −inf
@@ -572,7 +661,7 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
             for (int r = 0; r < 16; ++r) v[r] = vkey(r, h) >= nvalid ? kNegInf : 0.0f;
             return v;
           },
-          [&](const f32x16 (&sx)[2], typename Regs<T, D>::P& px) { weights_full<T, D>(sx, m, l, px, cs); },
+          l, m, cs,
           qr, oacc, w, lane);
     }
   } else {
@@ -625,10 +714,7 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
             for (int r = 0; r < 16; ++r) v[r] = ((dead >> vkey(r, h)) & 1u) ? kNegInf : 0.0f;
             return v;
           },
-          [&](const f32x16 (&sx)[2], typename Regs<T, D>::P& px) {
-            weights_full<T, D>(sx, m, asum, px, cs);
-          },
-          qr, oacc, w, lane);
+          asum, m, cs, qr, oacc, w, lane);
     } else {
       load_k<T, D>(a.kbp + head_ct * G::SUB_BYTES, w, lane, kc);
       load_v<T, D>(a.vbp + head_ct * G::SUB_BYTES, w, lane, vc);
