@@ -176,8 +176,10 @@ __device__ __forceinline__ void tile_weights(const f32x16 (&sacc)[2], const floa
   }
 }
 
-// Weights of a full exact sub-tile (no masks): P = 2^(Sᵀ·cs − m), row sums
-// taken from the rounded operands so numerator and denominator see the same P.
+// Weights of a full exact sub-tile (no masks): P = 2^(Sᵀ·cs − m) and the row
+// sums of its fp32 values. (The numerator takes P rounded to the operand type,
+// which is unbiased; summing the rounded values instead would need the packed
+// dot-product instruction, which stalls the matrix pipe on gfx950.)
 template <typename T, int D>
 __device__ __forceinline__ void weights_full(const f32x16 (&sacc)[2], const float (&m)[2],
                                              float (&l)[2], typename Regs<T, D>::P& pc, float cs) {
@@ -191,7 +193,8 @@ __device__ __forceinline__ void weights_full(const f32x16 (&sacc)[2], const floa
       for (int e = 0; e < G::KW; ++e)
         p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[qt][G::KW * c + e], cs, -m[qt]));
       pc[qt][c] = Op<T>::pack(p);
-      l[qt] = Op<T>::rowsum(pc[qt][c], l[qt]);
+#pragma unroll
+      for (int e = 0; e < G::KW; e += 2) l[qt] += p[e] + p[e + 1];
     }
   }
 }
@@ -212,7 +215,7 @@ __device__ __forceinline__ void interleave_tile() {
 // One software-pipelined sub-tile for bf16 operands, in an explicit order: the
 // MFMAs of PV(t) (Oᵀ += Vᵀ P(t)) and then of Sᵀ(t+2) (accumulated onto `init`)
 // alternate one by one with the weights of tile t+1 (P(t+1) = 2^(Sᵀ(t+1)·cs − m),
-// rounded and packed in pairs, each pair's sum added to acc). A V or K register
+// rounded and packed in pairs, their fp32 values added to acc). A V or K register
 // chunk is reloaded for two tiles ahead right after the last MFMA that reads it.
 // sched_barrier pins the order: with one wavefront per SIMD, the MFMA pipe and
 // the VALU only overlap where the instruction stream alternates, and the
@@ -241,7 +244,6 @@ __device__ __forceinline__ void xstep(typename Regs<bf16, D>::Acc& oacc,
   constexpr int NPV = 2 * NV, NM = NPV + 2 * G::NC;
   constexpr int EPM = 32 / NM;  // weights formed per MFMA
   static_assert(NM * EPM == 32, "32 weights per lane and sub-tile");
-  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
   uint32_t pw[2][4 * G::CPK];
   float pend = 0.f;
   sx[0] = init;
@@ -265,7 +267,7 @@ __device__ __forceinline__ void xstep(typename Regs<bf16, D>::Acc& oacc,
       const float p = __builtin_amdgcn_exp2f(fmaf(acc_read(sy[qt][r]), cs, -m[qt]));
       if (r & 1) {
         const bf16x2 pr = {(bf16)pend, (bf16)p};
-        acc[qt] = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc[qt], false);
+        acc[qt] += pend + p;
         pw[qt][r >> 1] = __builtin_bit_cast(uint32_t, pr);
       } else {
         pend = p;
