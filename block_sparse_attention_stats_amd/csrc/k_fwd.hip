@@ -44,6 +44,7 @@ constexpr float kNegInf = -__builtin_huge_valf();
 constexpr float kHeadroom = 64.0f;      // log2 headroom between the logit bound and the shift
 constexpr float kTinyDenom = 0x1p-60f;  // below this a tile goes to the careful kernel
 constexpr float kTau = 8.0f;            // careful kernel: log2 growth that raises the max
+constexpr int kCentroidsFirstBelow = 96;  // exact sub-tiles below which the centroid scan goes first
 
 enum TileKind { kExactFull = 0, kExactRagged = 1, kCentroid = 2 };
 
@@ -553,9 +554,9 @@ __device__ __forceinline__ void epilogue(const FwdArgs& a, typename Regs<T, D>::
 
 // The whole forward pass of one 64-row query tile (`item` = (bh, query block,
 // 64-row half of a 128-row block)).
-template <typename T, int D, bool CAREFUL, int SPB, bool DENSE>
+template <typename T, int D, bool CAREFUL, int SPB, bool DENSE, typename Before>
 __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShared<T, D>& sh,
-                                           typename Regs<T, D>::Xo& xo) {
+                                           typename Regs<T, D>::Xo& xo, const Before& before_exact) {
   using G = Geo<T, D>;
   constexpr int NC = G::NC, DT = G::DT, ESZ = G::ESZ, KW = G::KW;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
@@ -634,10 +635,58 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
   typename Regs<T, D>::K kc;  // careful kernel only
   typename Regs<T, D>::V vc;
 
+  // ---- phase 2: zeroth-order terms of the unselected blocks
+  auto phase2 = [&]() {
+    if (tail) {
+      const size_t head_ct = (size_t)bh * a.nct;
+      const float blk_w = (float)a.blk, last_w = (float)(a.n_last - a.blk);
+      if constexpr (!CAREFUL) {
+        // selected and padding centroids start at −inf, so they get weight 0;
+        // their row sums go to A_t, from which D gets n_j per centroid later
+        pipelined<T, D>(
+            a.nct, a.kbp, a.vbp, [&](int ct) -> size_t { return (head_ct + ct) * G::SUB_BYTES; },
+            [&](int ct) {
+              const int jbase = kSub * ct + 32 * w;
+              const int nvalid = a.n - jbase;  // valid centroids from this wavefront's first key
+              uint32_t dead = sh.selmask[jbase >> 5];
+              if (nvalid < 32) dead |= nvalid <= 0 ? ~0u : ~((1u << nvalid) - 1u);
+              f32x16 v;
+  #pragma unroll
+              for (int r = 0; r < 16; ++r) v[r] = ((dead >> vkey(r, h)) & 1u) ? kNegInf : 0.0f;
+              return v;
+            },
+            asum, m, cs, qr, oacc, w, lane);
+      } else {
+        load_k<T, D>(a.kbp + head_ct * G::SUB_BYTES, w, lane, kc);
+        load_v<T, D>(a.vbp + head_ct * G::SUB_BYTES, w, lane, vc);
+        for (int ct = 0; ct < a.nct; ++ct) {
+          const bool more = ct + 1 < a.nct;
+          const int jbase = kSub * ct + 32 * w;
+          const uint32_t word = sh.selmask[jbase >> 5];
+          const size_t nxt = (head_ct + ct + 1) * G::SUB_BYTES;
+          step<T, D, true, kCentroid>(oacc, qr, kc, vc, m, l, asum, cs, h, w, lane, a.n - kSub * ct,
+                                      word, a.n - 1 - jbase, blk_w, last_w,
+                                      more ? a.kbp + nxt : nullptr, more ? a.vbp + nxt : nullptr);
+        }
+      }
+    }
+  };
+
   // ---- phase 1: exact selected blocks, ascending
   const size_t head_sub = (size_t)bh * a.n * spb;
   const int nsub_last = (a.n_last + kSub - 1) / kSub;
   if constexpr (!CAREFUL) {
+    // With a fixed shift the order of the terms does not matter. For short
+    // exact sweeps the centroid scan comes first: it reads only the k̄ / ΣV
+    // tiles, which every query tile of the head shares, and fills the time a
+    // workgroup would otherwise spend in before_exact (the generation wait that
+    // lines up the exact sweeps over the gathered blocks). For long sweeps it
+    // comes last: measured at the Wan shape, the exact sweeps of a new
+    // generation then keep the L2 to themselves while the previous one scans
+    // centroids, which is worth more than the shorter wait.
+    const bool centroids_first = nsel * spb < kCentroidsFirstBelow;
+    if (centroids_first) phase2();
+    before_exact();
     // Full sub-tiles, software-pipelined two deep: Sᵀ of tile t+1 is issued
     // before the weights of tile t, so the MFMA pipe works while the VALU
     // exponentiates. The short last block (always last: indices ascend) is
@@ -666,6 +715,7 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
           l, m, cs,
           qr, oacc, w, lane);
     }
+    if (!centroids_first) phase2();
   } else {
     int s = 0, st = 0;
     int j = block_at(0);
@@ -695,41 +745,7 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
       st = st2;
       j = j2;
     }
-  }
-
-  // ---- phase 2: zeroth-order terms of the unselected blocks
-  if (tail) {
-    const size_t head_ct = (size_t)bh * a.nct;
-    const float blk_w = (float)a.blk, last_w = (float)(a.n_last - a.blk);
-    if constexpr (!CAREFUL) {
-      // selected and padding centroids start at −inf, so they get weight 0;
-      // their row sums go to A_t, from which D gets n_j per centroid later
-      pipelined<T, D>(
-          a.nct, a.kbp, a.vbp, [&](int ct) -> size_t { return (head_ct + ct) * G::SUB_BYTES; },
-          [&](int ct) {
-            const int jbase = kSub * ct + 32 * w;
-            const int nvalid = a.n - jbase;  // valid centroids from this wavefront's first key
-            uint32_t dead = sh.selmask[jbase >> 5];
-            if (nvalid < 32) dead |= nvalid <= 0 ? ~0u : ~((1u << nvalid) - 1u);
-            f32x16 v;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) v[r] = ((dead >> vkey(r, h)) & 1u) ? kNegInf : 0.0f;
-            return v;
-          },
-          asum, m, cs, qr, oacc, w, lane);
-    } else {
-      load_k<T, D>(a.kbp + head_ct * G::SUB_BYTES, w, lane, kc);
-      load_v<T, D>(a.vbp + head_ct * G::SUB_BYTES, w, lane, vc);
-      for (int ct = 0; ct < a.nct; ++ct) {
-        const bool more = ct + 1 < a.nct;
-        const int jbase = kSub * ct + 32 * w;
-        const uint32_t word = sh.selmask[jbase >> 5];
-        const size_t nxt = (head_ct + ct + 1) * G::SUB_BYTES;
-        step<T, D, true, kCentroid>(oacc, qr, kc, vc, m, l, asum, cs, h, w, lane, a.n - kSub * ct,
-                                    word, a.n - 1 - jbase, blk_w, last_w,
-                                    more ? a.kbp + nxt : nullptr, more ? a.vbp + nxt : nullptr);
-      }
-    }
+    phase2();
   }
 
   // fast kernel: D gets n_j per unselected block, i.e. blk·A_t, corrected for
@@ -787,17 +803,19 @@ __global__ __launch_bounds__(128, 1) void k_pisa_fwd(FwdArgs a) {
   __shared__ typename Regs<T, D>::Xo xo;
   const long item = blockIdx.x;
   const long g = item / a.nwg;
-  if (g > 0) {
-    if (threadIdx.x == 0) {
-      const int target = (int)(g * a.nwg - a.nwg / 10);
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target &&
-             __builtin_amdgcn_s_memrealtime() - t0 < (uint64_t)a.sync_ticks)
-        __builtin_amdgcn_s_sleep(2);
+  auto wait = [&]() {
+    if (g > 0) {
+      if (threadIdx.x == 0) {
+        const int target = (int)(g * a.nwg - a.nwg / 10);
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target &&
+               __builtin_amdgcn_s_memrealtime() - t0 < (uint64_t)a.sync_ticks)
+          __builtin_amdgcn_s_sleep(2);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-  }
-  query_tile<T, D, false, SPB, DENSE>(a, item, sh, xo);
+  };
+  query_tile<T, D, false, SPB, DENSE>(a, item, sh, xo, wait);
   __syncthreads();
   if (threadIdx.x == 0) __hip_atomic_fetch_add(a.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -811,7 +829,7 @@ __global__ __launch_bounds__(128, 1) void k_pisa_fwd_careful(FwdArgs a) {
   for (int e = blockIdx.x; e < count; e += gridDim.x) {
     const long item = a.redo[1 + e];
     __syncthreads();  // shared state of the previous tile fully consumed
-    query_tile<T, D, true, SPB, DENSE>(a, item, sh, xo);
+    query_tile<T, D, true, SPB, DENSE>(a, item, sh, xo, [] {});
   }
 }
 
