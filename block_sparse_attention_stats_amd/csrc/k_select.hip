@@ -7,9 +7,10 @@
 //   (n x n x D per head: small next to the fused pass). The sink column gets
 //   +infinity.
 // k_topk: one workgroup per score row, held in LDS as order-preserving 64-bit
-//   keys; an MSB-first radix select (8 passes of 8 bits) finds the k-th largest
-//   key T, then two block scans take every key > T and the lowest-index keys
-//   equal to T, and emit the indices ascending.
+//   keys; an MSB-first radix select (up to 8 passes of 8 bits) narrows down the
+//   k-th largest key T, stopping early once the bucket that holds it is to be
+//   taken whole; then two block scans take every key above it and the
+//   lowest-index keys equal to it, and emit the indices ascending.
 #include "pisa_dev.h"
 #include "pisa_internal.h"
 
@@ -94,7 +95,7 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
   extern __shared__ unsigned long long keys[];
   __shared__ int hist[256];
   __shared__ int wsum[4];
-  __shared__ int pick_digit, pick_gt;
+  __shared__ int pick_digit, pick_gt, pick_cnt;
   const int tid = threadIdx.x;
   const long row = blockIdx.x;
   const int n = a.n, k = a.topk;
@@ -124,23 +125,30 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
     if (gt < kk && kk <= incl) {
       pick_digit = dg;
       pick_gt = gt;
+      pick_cnt = c;
     }
     __syncthreads();
     prefix |= (unsigned long long)pick_digit << shift;
     pmask |= 255ull << shift;
     kk -= pick_gt;
+    const bool whole_bucket = (pick_cnt == kk);
     __syncthreads();
+    // every key left in the k-th key's bucket is selected: the remaining bits
+    // cannot change the set (and there is no tie to break)
+    if (whole_bucket) break;
   }
-  // prefix = T, the k-th largest key; take all keys > T and the kk lowest-index keys == T
+  // Keys whose digits so far exceed the prefix are selected, and of those equal
+  // to it the kk lowest-index ones (after all 8 passes: all keys > T, the k-th
+  // largest key, and the kk lowest-index keys == T).
   const int per = (n + 255) / 256, lo = min(n, tid * per), hi = min(n, lo + per);
   int ceq = 0;
-  for (int j = lo; j < hi; ++j) ceq += (keys[j] == prefix);
+  for (int j = lo; j < hi; ++j) ceq += ((keys[j] & pmask) == prefix);
   int eq_before = block_scan_incl(ceq, wsum) - ceq;
   int cnt = 0;
   {
     int r = eq_before;
     for (int j = lo; j < hi; ++j) {
-      const unsigned long long key = keys[j];
+      const unsigned long long key = keys[j] & pmask;
       const bool sel = key > prefix || (key == prefix && r++ < kk);
       cnt += sel;
     }
@@ -149,7 +157,7 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
   {
     int r = eq_before;
     for (int j = lo; j < hi; ++j) {
-      const unsigned long long key = keys[j];
+      const unsigned long long key = keys[j] & pmask;
       const bool sel = key > prefix || (key == prefix && r++ < kk);
       if (sel) out[pos++] = j;
     }
