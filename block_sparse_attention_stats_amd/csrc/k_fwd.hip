@@ -221,6 +221,18 @@ __device__ __forceinline__ void interleave_tile() {
 // sched_barrier pins the order: with one wavefront per SIMD, the MFMA pipe and
 // the VALU only overlap where the instruction stream alternates, and the
 // compiler's own schedule of this block leaves long runs of either kind.
+// A wavefront-uniform address, marked as such so that a load from it plus a
+// 32-bit lane offset takes the scalar-base form.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+using gbyte = const uint8_t __attribute__((address_space(1)));
+using gu32x4 = const u32x4 __attribute__((address_space(1)));
+__device__ __forceinline__ gbyte* sbase(const uint8_t* p) {
+  const uint64_t b = (uint64_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  return (gbyte*)(((uint64_t)hi << 32) | lo);
+}
+
 // One accumulator element into a VGPR, read where it is needed rather than as
 // part of a copy of the whole accumulator.
 __device__ __forceinline__ float acc_read(float x) {
@@ -247,6 +259,10 @@ __device__ __forceinline__ void xstep(typename Regs<bf16, D>::Acc& oacc,
   static_assert(NM * EPM == 32, "32 weights per lane and sub-tile");
   uint32_t pw[2][4 * G::CPK];
   float pend = 0.f;
+  // uniform base + 32-bit lane offset: the form global loads take with an SGPR
+  // base, which issues faster than a 64-bit address per lane
+  uint32_t lane_off = (uint32_t)lane * 16u;
+  asm volatile("" : "+v"(lane_off));  // keeps base + lane offset from being hoisted as one 64-bit value
   sx[0] = init;
   sx[1] = init;
 #pragma unroll
@@ -255,12 +271,12 @@ __device__ __forceinline__ void xstep(typename Regs<bf16, D>::Acc& oacc,
       const int x = mi >> 1, qt = mi & 1;
       Op<bf16>::mma(oacc[x / G::CPK][qt], vc[x], pc[qt][x % G::CPK]);
       if (qt == 1 && vnext != nullptr)
-        vc[x] = *(const uint4*)(vnext + ((w * NV + x) * kWave + lane) * 16);
+        vc[x] = __builtin_bit_cast(uint4, *(gu32x4*)(sbase(vnext + (size_t)((w * NV + x) * kWave * 16)) + lane_off));
     } else {
       const int c = (mi - NPV) >> 1, qt = (mi - NPV) & 1;
       Op<bf16>::mma(sx[qt], kc[c], qr[qt][c]);
       if (qt == 1 && knext != nullptr)
-        kc[c] = *(const uint4*)(knext + ((w * G::NC + c) * kWave + lane) * 16);
+        kc[c] = __builtin_bit_cast(uint4, *(gu32x4*)(sbase(knext + (size_t)((w * G::NC + c) * kWave * 16)) + lane_off));
     }
 #pragma unroll
     for (int u = 0; u < EPM; ++u) {
