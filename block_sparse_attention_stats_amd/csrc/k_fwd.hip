@@ -24,6 +24,13 @@
 //    gets n_j·p, N gets p·ΣV_j, and A_t accumulates p;
 //  * phase 3, first order: Uᵀ = H̄ᵀ Qᵀ on MFMA after the halves are summed,
 //    N += A_t · s · Uᵀ; then o = N / D.
+// With a fixed shift the order of phases 1 and 2 is free: short exact sweeps
+// scan the centroids first, long ones last (query_tile). Workgroups run in
+// generations of as many as are resident, and each lines up its exact sweep
+// with the others of its generation (k_pisa_fwd), so gathered blocks are
+// reused from the L2. For bf16 the sub-tile loop is written out in issue order
+// (xstep), since one wavefront per SIMD only overlaps MFMA and VALU work where
+// the instruction stream alternates them.
 //
 // The shift. Every logit obeys s q_t·k ≤ s ‖q_t‖ max‖k‖ (Cauchy–Schwarz; a
 // centroid's norm is at most the largest key norm), so with
@@ -62,9 +69,8 @@ struct Regs {
 
 template <typename T, int D>
 struct FwdShared {
-  uint32_t selmask[kMaxBlocks / 32];
-  float xstat[2][3][2][32];
-  uint4 q[2][Geo<T, D>::NC][kWave];  // query tile as B operands (fast kernel)
+  uint32_t selmask[kMaxBlocks / 32];  // selected blocks of the query tile, one bit each
+  float xstat[2][3][2][32];           // per-wavefront row statistics exchanged at the merge
 };
 
 template <typename T, int D>
@@ -97,22 +103,6 @@ __device__ __forceinline__ void mma_s(const typename Regs<T, D>::Q& qr,
   for (int c = 0; c < G::NC; ++c) {
     Op<T>::mma(sacc[0], kc[c], qr[0][c]);
     Op<T>::mma(sacc[1], kc[c], qr[1][c]);
-  }
-}
-
-// The same, with the query operands read from the LDS copy of the tile
-// (qs points at this lane's entry of chunk (0, 0)). Unused at present.
-template <typename T, int D>
-__device__ __forceinline__ void mma_s_lds(const uint4* qs, const typename Regs<T, D>::K& kc,
-                                          f32x16 (&sacc)[2], const f32x16& init) {
-  using G = Geo<T, D>;
-  sacc[0] = init;
-  sacc[1] = init;
-#pragma unroll
-  for (int c = 0; c < G::NC; ++c) {
-    const uint4 q0 = qs[c * kWave], q1 = qs[(G::NC + c) * kWave];
-    Op<T>::mma(sacc[0], kc[c], q0);
-    Op<T>::mma(sacc[1], kc[c], q1);
   }
 }
 
@@ -200,8 +190,9 @@ __device__ __forceinline__ void weights_full(const f32x16 (&sacc)[2], const floa
   }
 }
 
-// Scheduling hint for one pipelined tile: alternate the 32 MFMAs of PV(t) and
-// Sᵀ(t+2) with the VALU work of P(t+1), spreading the 16 loads among them.
+// Scheduling hint for one pipelined tile of fp32 operands (bf16 uses xstep):
+// alternate the MFMAs of PV(t) and Sᵀ(t+2) with the VALU work of P(t+1),
+// spreading the loads among them.
 __device__ __forceinline__ void interleave_tile() {
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
