@@ -82,7 +82,7 @@ def stats_bytes(B, H, L, D, block, esz) -> float:
     bh = B * H
     read = 3.0 * L * D * esz
     write = 2.0 * n * block * D * esz + 3.0 * n * D * 8 + 2.0 * (-(-n // 64)) * 64 * D * esz
-    cb = 1024 // block
+    cb = min(1024 // block, max(1, bh * n // 512))  # blocks per statistics run
     write += (-(-n // cb)) * D * D * 4
     return bh * (read + write)
 
@@ -126,6 +126,61 @@ def cpu_baseline(w, budget_s: float = 15.0) -> dict:
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def run_sweep(dev, args):
+    """Every point of the Wan-shape sweep (block x density x variant, batch 2) on
+    one set of inputs: per point the statistics, routing and fused-pass times
+    (HIP events, mean of 3 calls after one untimed call) and the fused pass's
+    credited TFLOP/s, next to the dense baseline on the same inputs."""
+    import torch
+
+    import block_sparse_attention_stats_amd as bsa
+    import synth
+
+    base = synth.SWEEP_BASE
+    t0 = time.time()
+    q, k, v = synth.make_qkv(base)
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    del q, k, v
+    print(f"[bench] sweep inputs on device ({time.time() - t0:.1f}s)", file=sys.stderr, flush=True)
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    od = torch.empty_like(qd)
+    dense_ms = timed(lambda: bsa.dense(qd, kd, vd, base.scale, out=od), reps=1)
+    dflops = 4.0 * base.B * base.H * float(base.L) * base.L * base.D
+    print(json.dumps({"sweep": "dense", "B": base.B, "H": base.H, "L": base.L, "D": base.D,
+                      "ms": dense_ms, "tflops": dflops / (dense_ms * 1e-3) / 1e12}), flush=True)
+    o = torch.empty_like(qd)
+    for w in synth.sweep():
+        n = w.n_blocks
+        topk = bsa.topk_from_density(w.density, n)
+        shape = bsa.make_shape(qd, w.block)
+        st = bsa.alloc_stats(shape, dev, want_mnorm=False)
+        idx = torch.empty((w.B, w.H, n, topk), dtype=torch.int32, device=dev)
+        hyd = w.variant == "hyd"
+        ms_stats = timed(lambda: bsa.block_stats(qd, kd, vd, w.block, out=st))
+        ms_sel = timed(lambda: bsa.select(st, topk, w.scale, 0.0, None, out=idx))
+        ms_fused = timed(lambda: bsa.attn_fwd(qd, st, idx, w.scale, hyd, out=o))
+        f = flops_from_idx(idx.cpu().numpy(), w.L, w.D, w.block, hyd)
+        ms_step = ms_stats + ms_sel + ms_fused
+        print(json.dumps({"sweep": w.name, "block": w.block, "density": w.density, "variant": w.variant,
+                          "topk": topk, "ms_stats": ms_stats, "ms_select": ms_sel, "ms_fused": ms_fused,
+                          "fused_tflops": f["total"] / (ms_fused * 1e-3) / 1e12,
+                          "exact_phase_mfma_frac": f["exact"] / (ms_fused * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
+                          "speedup_vs_dense_fused": dense_ms / ms_fused,
+                          "speedup_vs_dense_step": dense_ms / ms_step}), flush=True)
+        del st, idx
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -136,6 +191,9 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--sweep", action="store_true",
+                    help="instead of the headline step, time every block x density x variant "
+                         "point of the Wan-shape sweep (batch 2) and print one JSON line per point")
     ap.add_argument("--calib-copy", type=float, default=0.0, metavar="GIB",
                     help="only run one plain device-to-device copy of GIB GiB and exit: the "
                          "known-size kernel that scales the HBM byte counters")
@@ -158,6 +216,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"calib_copy_bytes": nbytes}), flush=True)
+        return
+
+    if args.sweep:
+        run_sweep(dev, args)
         return
 
     w = synth.WORKLOADS[args.workload]

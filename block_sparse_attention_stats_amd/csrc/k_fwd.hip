@@ -358,14 +358,16 @@ __device__ __forceinline__ void step(typename Regs<T, D>::Acc& oacc, const typen
 }
 
 // Software-pipelined loop over nt sub-tiles. off(t) gives tile t's byte offset
-// from kbase / vbase, init(t) the accumulator start of its Sᵀ, wts(Sᵀ, P) forms
-// its weights. Per tile t the MFMA pipe runs PV(t) then Sᵀ(t+2) while the VALU
-// forms P(t+1) from Sᵀ(t+1). K and V are double-buffered in registers: the
+// from kbase / vbase and init(t) the accumulator start of its Sᵀ; init_loop(t)
+// is the same for the tiles whose Sᵀ the main loop forms (t < nt - 2), where it
+// may be a constant. The weights' row sums go to acc. Per tile t the MFMA pipe
+// runs PV(t) then Sᵀ(t+2) while the VALU forms P(t+1) from Sᵀ(t+1). K and V are double-buffered in registers: the
 // loads of V(t+2) and K(t+4) are issued during tile t, two tiles before use,
 // which hides the latency of gathers that miss the L2.
-template <typename T, int D, bool LAG, typename Off, typename Init>
+template <typename T, int D, bool LAG, typename Off, typename InitL, typename Init>
 __device__ __forceinline__ void pipelined(int nt, const uint8_t* kbase, const uint8_t* vbase,
-                                          const Off& off, const Init& init, float (&acc)[2],
+                                          const Off& off, const InitL& init_loop, const Init& init,
+                                          float (&acc)[2],
                                           const float (&m)[2], float cs,
                                           const typename Regs<T, D>::Q& qr,
                                           typename Regs<T, D>::Acc& oacc, int w, int lane) {
@@ -381,6 +383,9 @@ __device__ __forceinline__ void pipelined(int nt, const uint8_t* kbase, const ui
   auto ldv = [&](typename Regs<T, D>::V& vc, int t) { load_v<T, D>(vbase + off(t), w, lane, vc); };
   auto sm = [&](const typename Regs<T, D>::K& kc, f32x16 (&sx)[2], int t) {
     mma_s<T, D>(qr, kc, sx, init(t));
+  };
+  auto sm_loop = [&](const typename Regs<T, D>::K& kc, f32x16 (&sx)[2], int t) {
+    mma_s<T, D>(qr, kc, sx, init_loop(t));
   };
   // The prologue has no conditions (tiles past the end are replaced by the
   // last one, and Sᵀ(1) of a one-tile run is never used), so that every path
@@ -401,20 +406,20 @@ __device__ __forceinline__ void pipelined(int nt, const uint8_t* kbase, const ui
   // vc0 = V(t), vc1 = V(t+1) (each where the tile exists)
   for (; t + 5 < nt; t += 2) {
     if constexpr (sizeof(T) == 2) {
-      xstep<D, LAG>(oacc, vc0, pa, kc0, qr, sa, init(t + 2), sb, pb, acc, m, cs, vbase + off(t + 2),
+      xstep<D, LAG>(oacc, vc0, pa, kc0, qr, sa, init_loop(t + 2), sb, pb, acc, m, cs, vbase + off(t + 2),
                kbase + off(t + 4), w, lane);  // PV(t), S(t+2), P(t+1)
-      xstep<D, LAG>(oacc, vc1, pb, kc1, qr, sb, init(t + 3), sa, pa, acc, m, cs, vbase + off(t + 3),
+      xstep<D, LAG>(oacc, vc1, pb, kc1, qr, sb, init_loop(t + 3), sa, pa, acc, m, cs, vbase + off(t + 3),
                kbase + off(t + 5), w, lane);  // PV(t+1), S(t+3), P(t+2)
     } else {
       mma_pv<T, D>(oacc, vc0, pa);  // PV(t)
       ldv(vc0, t + 2);
-      sm(kc0, sa, t + 2);           // S(t+2)
+      sm_loop(kc0, sa, t + 2);      // S(t+2)
       ldk(kc0, t + 4);
       wts(sb, pb);                  // P(t+1)
       interleave_tile();
       mma_pv<T, D>(oacc, vc1, pb);  // PV(t+1)
       ldv(vc1, t + 3);
-      sm(kc1, sb, t + 3);           // S(t+3)
+      sm_loop(kc1, sb, t + 3);      // S(t+3)
       ldk(kc1, t + 5);
       wts(sa, pa);                  // P(t+2)
       interleave_tile();
@@ -659,19 +664,19 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
       if constexpr (!CAREFUL) {
         // selected and padding centroids start at −inf, so they get weight 0;
         // their row sums go to A_t, from which D gets n_j per centroid later
+        auto cinit = [&](int ct) {
+          const int jbase = kSub * ct + 32 * w;
+          const int nvalid = a.n - jbase;  // valid centroids from this wavefront's first key
+          uint32_t dead = sh.selmask[jbase >> 5];
+          if (nvalid < 32) dead |= nvalid <= 0 ? ~0u : ~((1u << nvalid) - 1u);
+          f32x16 v;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] = ((dead >> vkey(r, h)) & 1u) ? kNegInf : 0.0f;
+          return v;
+        };
         pipelined<T, D, DENSE>(
             a.nct, a.kbp, a.vbp, [&](int ct) -> size_t { return (head_ct + ct) * G::SUB_BYTES; },
-            [&](int ct) {
-              const int jbase = kSub * ct + 32 * w;
-              const int nvalid = a.n - jbase;  // valid centroids from this wavefront's first key
-              uint32_t dead = sh.selmask[jbase >> 5];
-              if (nvalid < 32) dead |= nvalid <= 0 ? ~0u : ~((1u << nvalid) - 1u);
-              f32x16 v;
-  #pragma unroll
-              for (int r = 0; r < 16; ++r) v[r] = ((dead >> vkey(r, h)) & 1u) ? kNegInf : 0.0f;
-              return v;
-            },
-            asum, m, cs, qr, oacc, w, lane);
+            cinit, cinit, asum, m, cs, qr, oacc, w, lane);
       } else {
         load_k<T, D>(a.kbp + head_ct * G::SUB_BYTES, w, lane, kc);
         load_v<T, D>(a.vbp + head_ct * G::SUB_BYTES, w, lane, vc);
@@ -708,29 +713,26 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
     // exponentiates. The short last block (always last: indices ascend) is
     // left to the masked loop below.
     const bool ragged_last = a.n_last < a.blk && block_at(nsel - 1) == a.n - 1;
-    const int nt = (nsel - (ragged_last ? 1 : 0)) * spb;
+    // The short last block, if selected, is always last (indices ascend): its
+    // sub-tiles close the same pipeline, with keys beyond n_last starting at
+    // −inf. The main loop never forms Sᵀ of the last two sub-tiles, so its own
+    // initial value stays the constant zero.
+    const int nt_full = (nsel - (ragged_last ? 1 : 0)) * spb;
+    const int nt = nt_full + (ragged_last ? nsub_last : 0);
+    // (the short block is the selection's last entry, so the same formula
+    // addresses its sub-tiles)
     auto off = [&](int t) -> size_t {
       return (head_sub + (size_t)block_at(t / spb) * spb + (t % spb)) * G::SUB_BYTES;
     };
-    pipelined<T, D, DENSE>(
-        nt, a.kp, a.vp, off, [](int) { return f32x16{}; },
-        l, m, cs,
-        qr, oacc, w, lane);
-    if (ragged_last) {
-      // the short last block: keys beyond n_last start at −inf
-      const size_t base = (head_sub + (size_t)(a.n - 1) * spb) * G::SUB_BYTES;
-      pipelined<T, D, DENSE>(
-          nsub_last, a.kp + base, a.vp + base, [](int st) -> size_t { return (size_t)st * G::SUB_BYTES; },
-          [&](int st) {
-            const int nvalid = a.n_last - kSub * st - 32 * w;
-            f32x16 v;
+    auto init = [&](int t) {
+      const int nvalid = t < nt_full ? kSub : a.n_last - kSub * (t - nt_full) - 32 * w;
+      f32x16 v;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) v[r] = vkey(r, h) >= nvalid ? kNegInf : 0.0f;
-            return v;
-          },
-          l, m, cs,
-          qr, oacc, w, lane);
-    }
+      for (int r = 0; r < 16; ++r) v[r] = vkey(r, h) >= nvalid ? kNegInf : 0.0f;
+      return v;
+    };
+    pipelined<T, D, DENSE>(
+        nt, a.kp, a.vp, off, [](int) { return f32x16{}; }, init, l, m, cs, qr, oacc, w, lane);
     if (!centroids_first) phase2();
   } else {
     int s = 0, st = 0;

@@ -34,7 +34,11 @@ pisa_status_t check_shape(const pisa_shape_t* s, pisa::WsLayout* w) {
   w->n = (int)n;
   w->spb = s->block / 64;
   w->nct = (int)((n + 63) / 64);
-  w->cb = 1024 / s->block;
+  // Statistics run over runs of cb consecutive blocks, one workgroup each: up
+  // to 1024 tokens, fewer when that would leave fewer than ~512 workgroups to
+  // spread over the chip (short sequences).
+  const long cb_max = 1024 / s->block, by_size = bh * n / 512;
+  w->cb = (int)(by_size < 1 ? 1 : (by_size > cb_max ? cb_max : by_size));
   w->nch = (int)((n + w->cb - 1) / w->cb);
   w->esz = esz;
   const size_t sub = (size_t)64 * s->D * esz;

@@ -101,7 +101,8 @@ def redo_count(st, w) -> int:
     bh, n, spb = w.B * w.H, w.n_blocks, w.block // 64
     esz = 2 if w.dtype == "bf16" else 4
     kv = a256(bh * n * spb * 64 * w.D * esz)
-    nch = -(-n // (1024 // w.block))
+    cb = min(1024 // w.block, max(1, bh * n // 512))  # blocks per statistics run
+    nch = -(-n // cb)
     off = 2 * kv + a256(bh * nch * 4)
     return int(st.ws[off:off + 4].view(torch.int32).item())
 
