@@ -2,8 +2,9 @@
 // 2602.01077, section 2 "Covariance-Aware Routing"; the authors' README,
 // "Attention sink for MMDiT").
 //
-// k_scores: S_ij = scale * q̄_i·k̄_j + cov_weight * M_j in fp64 for 64x64 tiles
-//   of (query block, key block) pairs, a register-tiled fp64 GEMM through LDS
+// k_scores: S_ij = scale * q̄_i·k̄_j + cov_weight * M_j in fp64 for 128x128 (or,
+//   for small n, 64x64) tiles of (query block, key block) pairs, a
+//   register-tiled fp64 GEMM through LDS
 //   (n x n x D per head: small next to the fused pass). The sink column gets
 //   +infinity.
 // k_topk: one workgroup per score row, held in LDS as order-preserving 64-bit
@@ -16,49 +17,67 @@
 
 namespace pisa {
 
-template <int D>
+// k_scores tile: TM x TM (query block, key block) pairs per workgroup, each of
+// the 256 threads owning an (TM/16) x (TM/16) block of them. 128 for long
+// sequences (8 FMAs per LDS value read), 64 when n is small.
+template <int D, int TM>
 __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
-  __shared__ double As[16][65], Bs[16][65];
+  // Rows ty + 16x, columns tx + 16y. The dot products run over d in order, one
+  // fp64 FMA per term. The next chunk of q̄ / k̄ is read into registers while
+  // the current one is consumed from LDS.
+  constexpr int KC = 8, R = TM / 16, PER = TM * KC / 256;
+  __shared__ double As[KC][TM + 1], Bs[KC][TM + 1];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
   const long bh = blockIdx.z;
-  const int i0 = blockIdx.y * 64, j0 = blockIdx.x * 64;
+  const int i0 = blockIdx.y * TM, j0 = blockIdx.x * TM;
   const double* qb = a.qbar + (size_t)bh * a.n * D;
   const double* kb = a.kbar + (size_t)bh * a.n * D;
-  double acc[4][4];
+  double acc[R][R];
 #pragma unroll
-  for (int x = 0; x < 4; ++x)
+  for (int x = 0; x < R; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = 0.0;
-  for (int d0 = 0; d0 < D; d0 += 16) {
+    for (int y = 0; y < R; ++y) acc[x][y] = 0.0;
+  double pa[PER], pb[PER];
+  auto fetch = [&](int d0) {
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int x = tid + 256 * u, row = x >> 4, dd = x & 15;
-      As[dd][row] = (i0 + row < a.n) ? qb[(size_t)(i0 + row) * D + d0 + dd] : 0.0;
-      Bs[dd][row] = (j0 + row < a.n) ? kb[(size_t)(j0 + row) * D + d0 + dd] : 0.0;
+    for (int u = 0; u < PER; ++u) {
+      const int x = tid + 256 * u, row = x / KC, dd = x % KC;
+      pa[u] = (i0 + row < a.n) ? qb[(size_t)(i0 + row) * D + d0 + dd] : 0.0;
+      pb[u] = (j0 + row < a.n) ? kb[(size_t)(j0 + row) * D + d0 + dd] : 0.0;
+    }
+  };
+  fetch(0);
+  for (int d0 = 0; d0 < D; d0 += KC) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int x = tid + 256 * u, row = x / KC, dd = x % KC;
+      As[dd][row] = pa[u];
+      Bs[dd][row] = pb[u];
     }
     __syncthreads();
+    if (d0 + KC < D) fetch(d0 + KC);
 #pragma unroll
-    for (int dd = 0; dd < 16; ++dd) {
-      double av[4], bv[4];
+    for (int dd = 0; dd < KC; ++dd) {
+      double av[R], bv[R];
 #pragma unroll
-      for (int x = 0; x < 4; ++x) av[x] = As[dd][ty + 16 * x];
+      for (int x = 0; x < R; ++x) av[x] = As[dd][ty + 16 * x];
 #pragma unroll
-      for (int y = 0; y < 4; ++y) bv[y] = Bs[dd][tx + 16 * y];
+      for (int y = 0; y < R; ++y) bv[y] = Bs[dd][tx + 16 * y];
 #pragma unroll
-      for (int x = 0; x < 4; ++x)
+      for (int x = 0; x < R; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = fma(av[x], bv[y], acc[x][y]);
+        for (int y = 0; y < R; ++y) acc[x][y] = fma(av[x], bv[y], acc[x][y]);
     }
     __syncthreads();
   }
   double* out = a.scores + (size_t)bh * a.n * a.n;
 #pragma unroll
-  for (int y = 0; y < 4; ++y) {
+  for (int y = 0; y < R; ++y) {
     const int j = j0 + tx + 16 * y;
     if (j >= a.n) continue;
     const double cov = a.cov_weight != 0.0 ? a.cov_weight * a.mnorm[bh * a.n + j] : 0.0;
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
+    for (int x = 0; x < R; ++x) {
       const int i = i0 + ty + 16 * x;
       if (i >= a.n) continue;
       double sc = a.scale * acc[x][y];
@@ -96,6 +115,7 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
   __shared__ int hist[256];
   __shared__ int wsum[4];
   __shared__ int pick_digit, pick_gt, pick_cnt;
+  __shared__ unsigned long long red_and[4], red_or[4];
   const int tid = threadIdx.x;
   const long row = blockIdx.x;
   const int n = a.n, k = a.topk;
@@ -105,11 +125,37 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
     return;
   }
   const double* S = a.scores + row * (long)n;
-  for (int j = tid; j < n; j += 256) keys[j] = order_key(S[j]);
-
-  unsigned long long prefix = 0, pmask = 0;
+  unsigned long long kand = ~0ull, kor = 0ull;
+  for (int j = tid; j < n; j += 256) {
+    const unsigned long long key = order_key(S[j]);
+    keys[j] = key;
+    kand &= key;
+    kor |= key;
+  }
+  // Bits every key shares need no pass: start at the digit that holds the
+  // highest bit where keys differ (the leading digits of a row of scores,
+  // sign and exponent, are usually common, and histogramming them would pile
+  // every key onto one counter).
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    kand &= __shfl_xor(kand, o);
+    kor |= __shfl_xor(kor, o);
+  }
+  if ((tid & 63) == 0) {
+    red_and[tid >> 6] = kand;
+    red_or[tid >> 6] = kor;
+  }
+  __syncthreads();
+  kand = red_and[0] & red_and[1] & red_and[2] & red_and[3];
+  kor = red_or[0] | red_or[1] | red_or[2] | red_or[3];
+  const unsigned long long diff = kand ^ kor;
+  const int top = diff == 0 ? -1 : 63 - __builtin_clzll(diff);  // highest differing bit
+  const int first = top < 0 ? -8 : (top / 8) * 8;                // digit of the first pass
+  unsigned long long pmask = first + 8 >= 64 ? 0ull : ~((1ull << (first + 8)) - 1ull);
+  if (top < 0) pmask = ~0ull;
+  unsigned long long prefix = kand & pmask;
   int kk = k;
-  for (int shift = 56; shift >= 0; shift -= 8) {
+  for (int shift = first; shift >= 0; shift -= 8) {
     hist[tid] = 0;
     __syncthreads();
     for (int j = tid; j < n; j += 256) {
@@ -165,12 +211,17 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
 }
 
 hipError_t launch_scores(int D, const ScoreArgs& a, long bh, hipStream_t s) {
-  const unsigned t = (unsigned)((a.n + 63) / 64);
+  const bool big = a.n >= 512;
+  const int tm = big ? 128 : 64;
+  const unsigned t = (unsigned)((a.n + tm - 1) / tm);
   dim3 grid(t, t, (unsigned)bh);
-  if (D == 64)
-    hipLaunchKernelGGL((k_scores<64>), grid, dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((k_scores<128>), grid, dim3(256), 0, s, a);
+  if (D == 64) {
+    if (big) hipLaunchKernelGGL((k_scores<64, 128>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_scores<64, 64>), grid, dim3(256), 0, s, a);
+  } else {
+    if (big) hipLaunchKernelGGL((k_scores<128, 128>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_scores<128, 64>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
