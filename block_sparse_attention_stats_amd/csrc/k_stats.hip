@@ -22,7 +22,7 @@
 namespace pisa {
 
 template <typename T, int D, int MODE>
-__global__ __launch_bounds__(256) void k_block_stats(StatsArgs a) {
+__global__ __launch_bounds__(256, 2) void k_block_stats(StatsArgs a) {
   using G = Geo<T, D>;
   using O = Op<T>;
   constexpr int KW = G::KW, ESZ = G::ESZ, CPR = G::CPR, NC = G::NC, DT = G::DT, CPK = G::CPK;
@@ -75,7 +75,16 @@ __global__ __launch_bounds__(256) void k_block_stats(StatsArgs a) {
         }
   }
 
-  double csum[2] = {0.0, 0.0};  // column-sum tasks p = tid, tid + 256 over (tensor, d)
+  // Column sums, in fp64: task p = ((tensor * CG + g) << 2) | rq sums the KW
+  // columns of 16-byte group g over rows 16 rq .. 16 rq + 15 of each sub-tile
+  // (p = tid, tid + 256). The four row quarters of a group are adjacent lanes
+  // and are added together when the block is complete.
+  constexpr int CG = D / KW, NTASK = 3 * CG * 4, NU = (NTASK + 255) / 256;
+  double csum[NU][KW];
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int e = 0; e < KW; ++e) csum[u][e] = 0.0;
   float kn2max = 0.0f;          // largest squared key norm seen by this thread's rows
 
   uint4 pre[NT][PER];
@@ -119,14 +128,17 @@ __global__ __launch_bounds__(256) void k_block_stats(StatsArgs a) {
     // ---- fp64 column sums (q, k, v)
     if constexpr (MODE == kStatsFull) {
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < NU; ++u) {
         const int p = tid + 256 * u;
-        if (p < 3 * D) {
-          const int t = p / D, d = p % D;
-          double sacc = 0.0;
-          for (int row = 0; row < 64; ++row)
-            sacc += (double)O::to_f32(*(const T*)(&tile[t][row * PITCH + d * ESZ]));
-          csum[u] += sacc;
+        if (p < NTASK) {
+          const int t = (p >> 2) / CG, g = (p >> 2) % CG, rq = p & 3;
+#pragma unroll 4
+          for (int row = 16 * rq; row < 16 * rq + 16; ++row) {
+            const uint4 c = *(const uint4*)(&tile[t][row * PITCH + g * 16]);
+            const T* x = (const T*)&c;
+#pragma unroll
+            for (int e = 0; e < KW; ++e) csum[u][e] += (double)O::to_f32(x[e]);
+          }
         }
       }
     }
@@ -135,10 +147,16 @@ __global__ __launch_bounds__(256) void k_block_stats(StatsArgs a) {
     if constexpr (kDoPack) {
       const int row = tid >> 2, part = tid & 3;
       float ss = 0.0f;
-#pragma unroll 8
-      for (int d = part * (D / 4); d < (part + 1) * (D / 4); ++d) {
-        const float x = O::to_f32(*(const T*)(&tile[KT][row * PITCH + d * ESZ]));
-        ss = fmaf(x, x, ss);
+      constexpr int NCH = D / 4 / KW;  // 16-byte chunks in a quarter row
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        const uint4 ch16 = *(const uint4*)(&tile[KT][row * PITCH + (part * NCH + c) * 16]);
+        const T* x = (const T*)&ch16;
+#pragma unroll
+        for (int e = 0; e < KW; ++e) {
+          const float xf = O::to_f32(x[e]);
+          ss = fmaf(xf, xf, ss);
+        }
       }
       ss += __shfl_xor(ss, 1);
       ss += __shfl_xor(ss, 2);
@@ -205,25 +223,35 @@ __global__ __launch_bounds__(256) void k_block_stats(StatsArgs a) {
       uint8_t* kb_tile = a.kbp + ((size_t)bh * a.nct + ct) * G::SUB_BYTES;
       uint8_t* vb_tile = a.vbp + ((size_t)bh * a.nct + ct) * G::SUB_BYTES;
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
+      for (int u = 0; u < NU; ++u) {
         const int p = tid + 256 * u;
-        if (p < 3 * D) {
-          const int t = p / D, d = p % D;
-          const size_t o = ((size_t)bh * a.n + j) * D + d;
-          if (t == 0) {
-            a.qbar[o] = csum[u] / nj;
-          } else if (t == 1) {
-            const double kb = csum[u] / nj;
-            a.kbar[o] = kb;
-            kbf[d] = (float)kb;
-            *(T*)(kb_tile + kfmt_offset<T, D>(kk, d)) = O::from_f32((float)kb);
-          } else {
-            a.vsum[o] = csum[u];
-            vsf[d] = (float)csum[u];
-            *(T*)(vb_tile + vfmt_offset<T, D>(kk, d)) = O::from_f32((float)csum[u]);
-          }
-          csum[u] = 0.0;
+#pragma unroll
+        for (int e = 0; e < KW; ++e) {  // add the four row quarters (adjacent lanes)
+          csum[u][e] += __shfl_xor(csum[u][e], 1);
+          csum[u][e] += __shfl_xor(csum[u][e], 2);
         }
+        if (p < NTASK && (p & 3) == 0) {
+          const int t = (p >> 2) / CG, g = (p >> 2) % CG;
+#pragma unroll
+          for (int e = 0; e < KW; ++e) {
+            const int d = g * KW + e;
+            const size_t o = ((size_t)bh * a.n + j) * D + d;
+            if (t == 0) {
+              a.qbar[o] = csum[u][e] / nj;
+            } else if (t == 1) {
+              const double kb = csum[u][e] / nj;
+              a.kbar[o] = kb;
+              kbf[d] = (float)kb;
+              *(T*)(kb_tile + kfmt_offset<T, D>(kk, d)) = O::from_f32((float)kb);
+            } else {
+              a.vsum[o] = csum[u][e];
+              vsf[d] = (float)csum[u][e];
+              *(T*)(vb_tile + vfmt_offset<T, D>(kk, d)) = O::from_f32((float)csum[u][e]);
+            }
+          }
+        }
+#pragma unroll
+        for (int e = 0; e < KW; ++e) csum[u][e] = 0.0;
       }
       __syncthreads();
       // Σ_n (k_n − k̄_j)ᵀ v_n = G_j − k̄_j ⊗ ΣV_j
