@@ -115,7 +115,6 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
   __shared__ int hist[256];
   __shared__ int wsum[4];
   __shared__ int pick_digit, pick_gt, pick_cnt;
-  __shared__ unsigned long long red_and[4], red_or[4];
   const int tid = threadIdx.x;
   const long row = blockIdx.x;
   const int n = a.n, k = a.topk;
@@ -125,37 +124,10 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
     return;
   }
   const double* S = a.scores + row * (long)n;
-  unsigned long long kand = ~0ull, kor = 0ull;
-  for (int j = tid; j < n; j += 256) {
-    const unsigned long long key = order_key(S[j]);
-    keys[j] = key;
-    kand &= key;
-    kor |= key;
-  }
-  // Bits every key shares need no pass: start at the digit that holds the
-  // highest bit where keys differ (the leading digits of a row of scores,
-  // sign and exponent, are usually common, and histogramming them would pile
-  // every key onto one counter).
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    kand &= __shfl_xor(kand, o);
-    kor |= __shfl_xor(kor, o);
-  }
-  if ((tid & 63) == 0) {
-    red_and[tid >> 6] = kand;
-    red_or[tid >> 6] = kor;
-  }
-  __syncthreads();
-  kand = red_and[0] & red_and[1] & red_and[2] & red_and[3];
-  kor = red_or[0] | red_or[1] | red_or[2] | red_or[3];
-  const unsigned long long diff = kand ^ kor;
-  const int top = diff == 0 ? -1 : 63 - __builtin_clzll(diff);  // highest differing bit
-  const int first = top < 0 ? -8 : (top / 8) * 8;                // digit of the first pass
-  unsigned long long pmask = first + 8 >= 64 ? 0ull : ~((1ull << (first + 8)) - 1ull);
-  if (top < 0) pmask = ~0ull;
-  unsigned long long prefix = kand & pmask;
+  for (int j = tid; j < n; j += 256) keys[j] = order_key(S[j]);
+  unsigned long long prefix = 0, pmask = 0;
   int kk = k;
-  for (int shift = first; shift >= 0; shift -= 8) {
+  for (int shift = 56; shift >= 0; shift -= 8) {
     hist[tid] = 0;
     __syncthreads();
     for (int j = tid; j < n; j += 256) {
