@@ -807,14 +807,15 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
 
 // One workgroup per query tile, taken in order: consecutive workgroups work on
 // neighbouring query tiles of one head. Workgroups are grouped in generations
-// of nwg (as many as can be resident: two per CU); a workgroup of generation g
-// waits at its start until 90% of the workgroups of generation g-1 have
+// of nwg (as many as can be resident: two per CU); before its exact sweep a
+// workgroup of generation g waits until every workgroup of generation g-1 has
 // finished. Since workgroups are dispatched in index order, those are all
-// running by then; the wait keeps the resident workgroups' ascending sweeps
-// over the key blocks nearly in step, so one XCD's L2 serves each gathered K/V
-// tile to many of them (measured at the Wan shape with its scattered
-// selections: L2 hit rate 29% -> 42%+, fused pass ~25% faster). The wait only
-// shapes timing: it is bounded by sync_ticks, and no result depends on it.
+// running or done by then; the wait keeps the resident workgroups' ascending
+// sweeps over the key blocks in step, so one XCD's L2 serves each gathered K/V
+// tile to many of them. Measured with content-based selections: 27.5 -> 17.1 ms
+// at the Wan shape; waiting for all of the previous generation rather than 90%
+// of it took Hunyuan (larger heads) from 24.8 to 21.6 ms. The wait only shapes
+// timing: it is bounded by sync_ticks, and no result depends on it.
 template <typename T, int D, int SPB, bool DENSE>
 __global__ __launch_bounds__(128, 1) void k_pisa_fwd(FwdArgs a) {
   __shared__ FwdShared<T, D> sh;
@@ -824,7 +825,7 @@ __global__ __launch_bounds__(128, 1) void k_pisa_fwd(FwdArgs a) {
   auto wait = [&]() {
     if (g > 0) {
       if (threadIdx.x == 0) {
-        const int target = (int)(g * a.nwg - a.nwg / 10);
+        const int target = (int)(g * a.nwg);
         const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
         while (__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target &&
                __builtin_amdgcn_s_memrealtime() - t0 < (uint64_t)a.sync_ticks)
