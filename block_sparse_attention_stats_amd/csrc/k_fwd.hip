@@ -52,6 +52,8 @@ constexpr float kHeadroom = 64.0f;      // log2 headroom between the logit bound
 constexpr float kTinyDenom = 0x1p-60f;  // below this a tile goes to the careful kernel
 constexpr float kTau = 8.0f;            // careful kernel: log2 growth that raises the max
 constexpr int kCentroidsFirstBelow = 96;  // exact sub-tiles below which the centroid scan goes first
+constexpr int kEarlySignalMaxCt = 24;     // centroid tiles up to which a workgroup counts as done
+                                          // for the generation wait once its exact sweep ends
 
 enum TileKind { kExactFull = 0, kExactRagged = 1, kCentroid = 2 };
 
@@ -575,9 +577,10 @@ __device__ __forceinline__ void epilogue(const FwdArgs& a, typename Regs<T, D>::
 
 // The whole forward pass of one 64-row query tile (`item` = (bh, query block,
 // 64-row half of a 128-row block)).
-template <typename T, int D, bool CAREFUL, int SPB, bool DENSE, typename Before>
+template <typename T, int D, bool CAREFUL, int SPB, bool DENSE, typename Before, typename After>
 __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShared<T, D>& sh,
-                                           typename Regs<T, D>::Xo& xo, const Before& before_exact) {
+                                           typename Regs<T, D>::Xo& xo, const Before& before_exact,
+                                           const After& after_exact) {
   using G = Geo<T, D>;
   constexpr int NC = G::NC, DT = G::DT, ESZ = G::ESZ, KW = G::KW;
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
@@ -588,7 +591,10 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
   const int i = (int)(rest % a.n);
   const long bh = rest / a.n;
   const int r0 = i * a.blk + half * kSub;
-  if (r0 >= a.L) return;
+  if (r0 >= a.L) {
+    after_exact();
+    return;
+  }
 
   constexpr bool dense = DENSE;
   const int nsel = dense ? a.n : a.topk;
@@ -733,6 +739,7 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
     };
     pipelined<T, D, DENSE>(
         nt, a.kp, a.vp, off, [](int) { return f32x16{}; }, init, l, m, cs, qr, oacc, w, lane);
+    after_exact();
     if (!centroids_first) phase2();
   } else {
     int s = 0, st = 0;
@@ -808,14 +815,23 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
 // One workgroup per query tile, taken in order: consecutive workgroups work on
 // neighbouring query tiles of one head. Workgroups are grouped in generations
 // of nwg (as many as can be resident: two per CU); before its exact sweep a
-// workgroup of generation g waits until every workgroup of generation g-1 has
-// finished. Since workgroups are dispatched in index order, those are all
-// running or done by then; the wait keeps the resident workgroups' ascending
-// sweeps over the key blocks in step, so one XCD's L2 serves each gathered K/V
-// tile to many of them. Measured with content-based selections: 27.5 -> 17.1 ms
-// at the Wan shape; waiting for all of the previous generation rather than 90%
-// of it took Hunyuan (larger heads) from 24.8 to 21.6 ms. The wait only shapes
-// timing: it is bounded by sync_ticks, and no result depends on it.
+// workgroup of generation g waits until every workgroup of generation g-1 is
+// done with its exact sweep. Since workgroups are dispatched in index order,
+// those are all running or done by then; the wait keeps the resident
+// workgroups' ascending sweeps over the key blocks in step, so one XCD's L2
+// serves each gathered K/V tile to many of them. Measured with content-based
+// selections at the Wan shape: 27.5 -> 17.1 ms; waiting for all of the previous
+// generation rather than 90% of it took Hunyuan from 24.8 to 21.6 ms.
+//
+// "Done" is counted in one of two places. Where the centroid scan is short
+// (at most kEarlySignalMaxCt tiles), wavefront 0 counts its workgroup right
+// after the exact sweep, so the next generation's sweeps overlap this one's
+// centroid scans: 17.1 -> 16.7 ms at Wan. Those next-generation workgroups
+// whose slot is still held by a centroid scan start late, though, and the lag
+// grows with the scan: with 30 or more centroid tiles (Hunyuan, or Wan at twice
+// its length) the sweeps drift apart and the pass gets 1-4% slower, so there a
+// workgroup counts only once it has finished. The wait only shapes timing: it
+// is bounded by sync_ticks, and no result depends on it.
 template <typename T, int D, int SPB, bool DENSE>
 __global__ __launch_bounds__(128, 1) void k_pisa_fwd(FwdArgs a) {
   __shared__ FwdShared<T, D> sh;
@@ -834,9 +850,17 @@ __global__ __launch_bounds__(128, 1) void k_pisa_fwd(FwdArgs a) {
       __syncthreads();
     }
   };
-  query_tile<T, D, false, SPB, DENSE>(a, item, sh, xo, wait);
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_fetch_add(a.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  auto done = [&]() {
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(a.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  const bool early = a.nct <= kEarlySignalMaxCt;
+  query_tile<T, D, false, SPB, DENSE>(a, item, sh, xo, wait, [&] {
+    if (early) done();
+  });
+  if (!early) {
+    __syncthreads();
+    done();
+  }
 }
 
 // Recomputes, with a running maximum, the query tiles the fast kernel queued.
@@ -848,7 +872,7 @@ __global__ __launch_bounds__(128, 1) void k_pisa_fwd_careful(FwdArgs a) {
   for (int e = blockIdx.x; e < count; e += gridDim.x) {
     const long item = a.redo[1 + e];
     __syncthreads();  // shared state of the previous tile fully consumed
-    query_tile<T, D, true, SPB, DENSE>(a, item, sh, xo, [] {});
+    query_tile<T, D, true, SPB, DENSE>(a, item, sh, xo, [] {}, [] {});
   }
 }
 
