@@ -23,7 +23,11 @@ section; "gist" = the gist.science technical summary of arXiv 2602.01077,
 6. o_t = N_t / D_t with the exact terms of the selected blocks, the zeroth-order
    terms α_tj = exp(s q_t·k̄_j) of the unselected ones and, for the hybrid
    variant, the global first-order term (gist, "Core Algorithm", N_t equation;
-   README, "Kernel variants" for the zeroth-order-only variant).
+   README, "Kernel variants" for the zeroth-order-only variant). The per-block
+   first-order variant ("pb1") gives every unselected block its own first-order
+   term α_tj·s·q_t H_j instead: the distinct per-block terms the gist's "Core
+   Algorithm" replaces by the global mean H̄, and the first-order variant the
+   atlas summary's results compare against.
 
 Readings where the pages are silent or garbled (each is listed in the design doc):
   * the softmax scale s (default 1/√D) multiplies every logit and the first-order
@@ -140,7 +144,7 @@ def select_topk(S: np.ndarray, topk: int) -> np.ndarray:
 
 
 def pisa_rows(q, k, v, st: dict, idx_i: np.ndarray, i: int, block: int, scale: float,
-              first_order: bool):
+              first_order: bool, per_block: bool = False):
     """N_t, D_t and the shift m_t for every query row t of query block i.
 
     gist, "Core Algorithm": N_t = Σ_{S_i} Σ_n e^{ℓ_tn} v_n + Σ_{U_i} α_tj ΣV_j
@@ -148,6 +152,11 @@ def pisa_rows(q, k, v, st: dict, idx_i: np.ndarray, i: int, block: int, scale: f
     zeroth-order terms without the values, n_j α_tj for a block of n_j tokens.
     Every exponent is shifted by the row maximum m_t; the unshifted values are
     N_t·e^{m_t} and D_t·e^{m_t}.
+
+    per_block (instead of first_order): each unselected block's own first-order
+    term Σ_{U_i} α_tj s q_t H_j, the term that the global H̄ stands in for. D_t is
+    the same, since the first-order part of a block's denominator is
+    α_tj s q_t Σ_n (k_n − k̄_j) = 0.
     """
     L = q.shape[0]
     n = st["kbar"].shape[0]
@@ -173,6 +182,9 @@ def pisa_rows(q, k, v, st: dict, idx_i: np.ndarray, i: int, block: int, scale: f
         Nt = Nt + alpha @ st["vsum"][uns]
         if first_order:
             Nt = Nt + alpha.sum(axis=1)[:, None] * scale * (Qi @ st["Hbar"])
+        elif per_block:
+            for u, j in enumerate(uns):
+                Nt = Nt + alpha[:, u:u + 1] * scale * (Qi @ st["H"][j])
     return Nt, Dt, m
 
 
@@ -194,8 +206,8 @@ def head_forward(q, k, v, *, block: int, topk: int, scale: float, variant: str =
     the output to those query blocks (other rows are NaN). Returns (o, idx) or
     (o, idx, stats, scores).
     """
-    if variant not in ("hyd", "0th"):
-        raise ValueError("variant must be 'hyd' or '0th'")
+    if variant not in ("hyd", "0th", "pb1"):
+        raise ValueError("variant must be 'hyd', '0th' or 'pb1'")
     L, D = q.shape
     st = block_stats(q, k, v, block)
     n = st["kbar"].shape[0]
@@ -206,7 +218,8 @@ def head_forward(q, k, v, *, block: int, topk: int, scale: float, variant: str =
         idx = select_topk(S, topk)
     o = np.full((L, D), np.nan)
     for i in (range(n) if qblocks is None else qblocks):
-        Nt, Dt, _ = pisa_rows(q, k, v, st, idx[i], i, block, scale, variant == "hyd")
+        Nt, Dt, _ = pisa_rows(q, k, v, st, idx[i], i, block, scale, variant == "hyd",
+                              variant == "pb1")
         o[i * block:min(L, (i + 1) * block)] = Nt / Dt[:, None]
     if want_stats:
         return o, idx, st, S
@@ -243,10 +256,12 @@ def dense_attention(q, k, v, scale=None, chunk: int = 1024):
     return o
 
 
-def effective_flops(L: int, D: int, block: int, idx: np.ndarray, first_order: bool) -> float:
+def effective_flops(L: int, D: int, block: int, idx: np.ndarray, first_order: bool,
+                    per_block: bool = False) -> float:
     """Credited FLOPs of the fused pass for one (batch, head): 4·D per exact
     (query, key) pair, 4·D per (query, unselected block) pair, and 2·D² per query
-    row for the first-order term when its query block has unselected blocks."""
+    row for the first-order term when its query block has unselected blocks
+    (per_block: 2·D² per (query, unselected block) pair instead)."""
     sizes = block_sizes(L, block)
     n = sizes.size
     total = 0.0
@@ -257,4 +272,6 @@ def effective_flops(L: int, D: int, block: int, idx: np.ndarray, first_order: bo
         total += nq * (4.0 * D * exact + 4.0 * D * nu)
         if first_order and nu > 0:
             total += 2.0 * nq * D * D
+        if per_block:
+            total += 2.0 * nq * D * D * nu
     return total

@@ -95,7 +95,7 @@ def test_worked_example_outputs(golden):
 
 # --------------------------------------------------------------------------- P1
 @pytest.mark.parametrize("L,D,block", [(256, 16, 64), (200, 8, 64), (300, 32, 128), (37, 4, 8)])
-@pytest.mark.parametrize("variant", ["hyd", "0th"])
+@pytest.mark.parametrize("variant", ["hyd", "0th", "pb1"])
 def test_density_one_is_dense(L, D, block, variant):
     q, k, v = rand_head(L, D, seed=L + D)
     s = 1.0 / math.sqrt(D)
@@ -119,7 +119,7 @@ def constant_key_head(L, D, block, seed):
 
 
 @pytest.mark.parametrize("sink", [None, 0, -1])
-@pytest.mark.parametrize("variant", ["hyd", "0th"])
+@pytest.mark.parametrize("variant", ["hyd", "0th", "pb1"])
 @pytest.mark.parametrize("L,block,topk", [(256, 32, 2), (250, 32, 3), (77, 16, 1)])
 def test_constant_key_blocks_are_exact(sink, variant, L, block, topk):
     """Constant keys in every block: H_j = 0, H̄ = 0, α_tj e^{0} exact, so the
@@ -136,7 +136,8 @@ def test_constant_key_blocks_are_exact(sink, variant, L, block, topk):
 
 def test_constant_unselected_blocks_only_zeroth_exact():
     """Only the unselected blocks have constant keys: the zeroth-order variant is
-    exact, the hybrid is not (its H̄ averages the selected blocks' H_j too)."""
+    exact, the hybrid is not (its H̄ averages the selected blocks' H_j too), and
+    the per-block first-order variant is exact as well (its H_j are all 0)."""
     L, D, block = 192, 8, 32
     rng = np.random.default_rng(7)
     q, k, v = rand_head(L, D, seed=7)
@@ -150,7 +151,9 @@ def test_constant_unselected_blocks_only_zeroth_exact():
     dense = sdpa(q, k, v, s)
     o0, _ = oracle.head_forward(q, k, v, block=block, topk=2, scale=s, variant="0th", idx=idx)
     oh, _ = oracle.head_forward(q, k, v, block=block, topk=2, scale=s, variant="hyd", idx=idx)
+    op, _ = oracle.head_forward(q, k, v, block=block, topk=2, scale=s, variant="pb1", idx=idx)
     np.testing.assert_allclose(o0, dense, atol=1e-12)
+    np.testing.assert_allclose(op, dense, atol=1e-12)
     assert np.abs(oh - dense).max() > 1e-6
 
 
@@ -160,7 +163,7 @@ def test_constant_values():
     q, k, _ = rand_head(L, D, 3)
     c = np.linspace(-1, 2, D)
     v = np.tile(c, (L, 1))
-    for variant in ("hyd", "0th"):
+    for variant in ("hyd", "0th", "pb1"):
         o, _ = oracle.head_forward(q, k, v, block=block, topk=2, scale=0.4, variant=variant, sink_idx=-1)
         np.testing.assert_allclose(o, v, atol=1e-12)
 
@@ -222,14 +225,46 @@ def test_taylor_orders():
     for eps in (2e-2, 1e-2, 5e-3):
         k = np.repeat(c, block, axis=0) + eps * np.tile(delta, (n, 1))
         dense = sdpa(q, k, v, 0.7)
-        for var in ("hyd", "0th"):
+        for var in ("hyd", "0th", "pb1"):
             o, _ = oracle.head_forward(q, k, v, block=block, topk=1, scale=0.7, variant=var, idx=idx)
             errs[(var, eps)] = np.abs(o - dense).max()
+            if var == "pb1":  # every H_j equals H̄ here, so the two first-order terms agree
+                oh, _ = oracle.head_forward(q, k, v, block=block, topk=1, scale=0.7, variant="hyd", idx=idx)
+                np.testing.assert_allclose(o, oh, atol=1e-13)
     for e1, e2 in ((2e-2, 1e-2), (1e-2, 5e-3)):
         r_h = errs[("hyd", e1)] / errs[("hyd", e2)]
         r_0 = errs[("0th", e1)] / errs[("0th", e2)]
         assert 3.5 < r_h < 4.5, r_h
         assert 1.8 < r_0 < 2.2, r_0
+
+
+def test_taylor_orders_distinct_blocks():
+    """The same ε-scaling with a different δ pattern (hence a different H_j) in
+    every block: the global H̄ no longer matches any block, so the hybrid drops to
+    first order, while the per-block first-order variant stays second order
+    (gist, "Core Algorithm": the distinct per-block first-order terms that H̄
+    replaces)."""
+    D, block, n = 4, 8, 4
+    L = block * n
+    rng = np.random.default_rng(21)
+    delta = rng.normal(size=(n, block, D))
+    delta -= delta.mean(axis=1, keepdims=True)
+    v = rng.normal(size=(L, D))
+    c = rng.normal(size=(n, D))
+    q = rng.normal(size=(L, D))
+    idx = np.tile(np.array([0]), (n, 1))
+    errs = {}
+    for eps in (2e-2, 1e-2, 5e-3):
+        k = np.repeat(c, block, axis=0) + eps * delta.reshape(L, D)
+        dense = sdpa(q, k, v, 0.7)
+        for var in ("hyd", "pb1"):
+            o, _ = oracle.head_forward(q, k, v, block=block, topk=1, scale=0.7, variant=var, idx=idx)
+            errs[(var, eps)] = np.abs(o - dense).max()
+    for e1, e2 in ((2e-2, 1e-2), (1e-2, 5e-3)):
+        r_h = errs[("hyd", e1)] / errs[("hyd", e2)]
+        r_p = errs[("pb1", e1)] / errs[("pb1", e2)]
+        assert 1.8 < r_h < 2.3, r_h
+        assert 3.5 < r_p < 4.5, r_p
 
 
 # --------------------------------------------------------------------------- P9
@@ -246,18 +281,51 @@ def test_global_mean_replacement_identity_and_bound():
     for i in range(n):
         rows = slice(i * block, min(L, (i + 1) * block))
         Nh, Dh, m = oracle.pisa_rows(q, k, v, st, idx[i], i, block, s, True)
+        Npb, Dpb, mpb = oracle.pisa_rows(q, k, v, st, idx[i], i, block, s, False, per_block=True)
+        np.testing.assert_array_equal(m, mpb)
+        np.testing.assert_allclose(Dpb, Dh, rtol=1e-15)
         uns = [j for j in range(n) if j not in set(idx[i])]
-        # independent per-block first-order numerator, written here from the Taylor expansion
-        Npb = oracle.pisa_rows(q, k, v, st, idx[i], i, block, s, False)[0].copy()
         diff = np.zeros_like(Npb)
         bound = np.zeros(Npb.shape[0])
         for j in uns:
             a = np.exp(s * q[rows] @ st["kbar"][j] - m)
-            Npb += a[:, None] * s * (q[rows] @ st["H"][j])
             diff += a[:, None] * s * (q[rows] @ (st["Hbar"] - st["H"][j]))
             bound += a * s * np.linalg.norm(q[rows], axis=1) * M[j]
         np.testing.assert_allclose(Nh - Npb, diff, atol=1e-12)
         assert np.all(np.linalg.norm(Nh - Npb, axis=1) <= bound + 1e-12)
+
+
+@pytest.mark.parametrize("L,block,topk", [(160, 32, 2), (150, 32, 1), (100, 16, 3)])
+def test_per_block_first_order_from_the_keys(L, block, topk):
+    """The per-block first-order term expanded over the block's own keys:
+    α_tj s q_t H_j = Σ_n α_tj (ℓ_tn − c_tj) v_n with ℓ_tn = s q_t·k_n and
+    c_tj = s q_t·k̄_j, so an unselected block contributes Σ_n α_tj (1 + ℓ_tn − c_tj) v_n
+    to N_t (first-order Taylor expansion of e^{ℓ_tn} about c_tj, gist "Core
+    Algorithm"). Computed here from q, k, v alone, without H_j; the ragged last
+    block (L not a multiple of the block) uses its actual keys."""
+    D = 6
+    q, k, v = rand_head(L, D, L + topk)
+    s = 0.55
+    o, idx, st, _ = oracle.head_forward(q, k, v, block=block, topk=topk, scale=s, variant="pb1",
+                                        want_stats=True)
+    n = st["kbar"].shape[0]
+    for i in range(n):
+        rows = slice(i * block, min(L, (i + 1) * block))
+        Qi = q[rows]
+        m = oracle.pisa_rows(q, k, v, st, idx[i], i, block, s, False, per_block=True)[2]
+        N = np.zeros((Qi.shape[0], D))
+        Dn = np.zeros(Qi.shape[0])
+        for j in range(n):
+            Kj, Vj = k[j * block:min(L, (j + 1) * block)], v[j * block:min(L, (j + 1) * block)]
+            ell = s * Qi @ Kj.T
+            if j in set(idx[i]):
+                w = np.exp(ell - m[:, None])
+            else:
+                c = s * Qi @ Kj.mean(axis=0)
+                w = np.exp(c - m)[:, None] * (1.0 + ell - c[:, None])
+            N += w @ Vj
+            Dn += w.sum(axis=1)
+        np.testing.assert_allclose(o[rows], N / Dn[:, None], atol=1e-12)
 
 
 # --------------------------------------------------------------------------- P10-P12
