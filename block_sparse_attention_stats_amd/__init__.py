@@ -204,17 +204,29 @@ def select(st: Stats, topk: int, scale: float, cov_weight: float = 0.0, sink_idx
     return idx
 
 
-def attn_fwd(q, st: Stats, idx: torch.Tensor, scale: float, first_order: bool = True,
+VARIANTS = {"0th": 0, "hyd": 1, "pb1": 2}
+
+
+def attn_fwd(q, st: Stats, idx: torch.Tensor, scale: float, first_order=True,
              out: torch.Tensor | None = None) -> torch.Tensor:
-    """Step 3: fused exact + zeroth-order (+ global first-order) pass."""
+    """Step 3: fused exact + zeroth-order (+ first-order) pass.
+
+    first_order: True or "hyd" (global H̄ term), False or "0th" (none), "pb1"
+    (each unselected block's own first-order term)."""
     _check_qkv(q)
+    if isinstance(first_order, str):
+        if first_order not in VARIANTS:
+            raise ValueError(f"unknown variant {first_order!r}; expected one of {sorted(VARIANTS)}")
+        code = VARIANTS[first_order]
+    else:
+        code = 1 if first_order else 0
     if idx.dtype != torch.int32 or not idx.is_contiguous() or not idx.is_cuda:
         raise ValueError("idx must be a contiguous int32 GPU tensor")
     shape = st.shape
     o = out if out is not None else torch.empty_like(q)
     sst = st.struct()
     _check(load_library().pisa_attn_fwd(ctypes.byref(shape), q.data_ptr(), ctypes.byref(sst),
-                                        1 if first_order else 0, idx.data_ptr(), int(idx.shape[-1]),
+                                        code, idx.data_ptr(), int(idx.shape[-1]),
                                         float(scale), o.data_ptr(), _stream()), "pisa_attn_fwd")
     return o
 
@@ -258,6 +270,15 @@ def piecewise_sparse_attention_0th(q, k, v, density: float = 0.15, block_size: i
     """PISA forward, zeroth-order-only variant (no global first-order term)."""
     return piecewise_sparse_attention_hyd(q, k, v, density, block_size, sink_idx, cov_weight, scale,
                                           first_order=False, return_idx=return_idx)
+
+
+def piecewise_sparse_attention_pb1(q, k, v, density: float = 0.15, block_size: int = 64,
+                                   sink_idx=None, cov_weight: float = 0.0, scale=None,
+                                   return_idx: bool = False):
+    """PISA forward with a first-order term per unselected block (q·H_j for each
+    block instead of the global H̄); costs about as much as dense attention."""
+    return piecewise_sparse_attention_hyd(q, k, v, density, block_size, sink_idx, cov_weight, scale,
+                                          first_order="pb1", return_idx=return_idx)
 
 
 piecewise_sparse_attention = piecewise_sparse_attention_hyd

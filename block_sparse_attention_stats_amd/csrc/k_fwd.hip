@@ -810,6 +810,296 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
     epilogue<T, D, CAREFUL, 1>(a, oacc, m, l, asum, qr, sh, xo, tail, bh, r0, lane, item);
 }
 
+// ---------------------------------------------------------------------------
+// Per-block first-order variant. An unselected block j contributes
+// α_tj (ΣV_j + s q_t H_j) to N_t, which expands over the block's own keys as
+// Σ_n α_tj (1 + s q_t·(k_n − k̄_j)) v_n: the first-order Taylor expansion of
+// e^{ℓ_tn} about the centroid logit. So the variant is one sweep over every
+// key block with linear weights P = α_tj (1 + ℓ_tn − c_tj) on the unselected
+// blocks and exponential ones on the selected blocks, on the same MFMA operand
+// copies of K and V; no D×D matrix per block is stored or read. The centroid
+// logits c_tj come from the k̄ tiles, 64 blocks at a time, through LDS.
+
+// Linear weights of one sub-tile of an unselected block: P = a1·Sᵀ + b1 per
+// query row (a1 = α s, b1 = α (1 − s C)), and their row sums. RAGGED: keys past
+// the end of the sequence carry −inf in Sᵀ and get weight 0.
+template <typename T, int D, bool RAGGED>
+__device__ __forceinline__ void weights_linear(const f32x16 (&sacc)[2], const float (&a1)[2],
+                                               const float (&b1)[2], float (&l)[2],
+                                               typename Regs<T, D>::P& pc) {
+  using G = Geo<T, D>;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+    for (int c = 0; c < G::CPK; ++c) {
+      float p[G::KW];
+#pragma unroll
+      for (int e = 0; e < G::KW; ++e) {
+        const float sv = sacc[qt][G::KW * c + e];
+        const float x = fmaf(sv, a1[qt], b1[qt]);
+        p[e] = (RAGGED && sv == kNegInf) ? 0.0f : x;
+      }
+      pc[qt][c] = Op<T>::pack(p);
+#pragma unroll
+      for (int e = 0; e < G::KW; e += 2) l[qt] += p[e] + p[e + 1];
+    }
+  }
+}
+
+// Software-pipelined sweep over nt sub-tiles with per-tile weights wts(Sᵀ, P, t)
+// (same schedule as the generic path of `pipelined`: PV(t) and Sᵀ(t+2) on the
+// MFMA pipe while the VALU forms P(t+1); K and V double-buffered two tiles
+// ahead; loads past the end clamped to the last tile).
+template <typename T, int D, typename Off, typename Init, typename Wts>
+__device__ __forceinline__ void pipelined_w(int nt, const uint8_t* kbase, const uint8_t* vbase,
+                                            const Off& off, const Init& init, const Wts& wts,
+                                            const typename Regs<T, D>::Q& qr,
+                                            typename Regs<T, D>::Acc& oacc, int w, int lane) {
+  if (nt <= 0) return;
+  typename Regs<T, D>::K kc0, kc1;
+  typename Regs<T, D>::V vc0, vc1;
+  f32x16 sa[2], sb[2];
+  typename Regs<T, D>::P pa, pb;
+  auto ldk = [&](typename Regs<T, D>::K& kc, int t) { load_k<T, D>(kbase + off(t), w, lane, kc); };
+  auto ldv = [&](typename Regs<T, D>::V& vc, int t) { load_v<T, D>(vbase + off(t), w, lane, vc); };
+  auto sm = [&](const typename Regs<T, D>::K& kc, f32x16 (&sx)[2], int t) {
+    mma_s<T, D>(qr, kc, sx, init(t));
+  };
+  const int tl = nt - 1;
+  ldk(kc0, 0);
+  ldv(vc0, 0);
+  ldk(kc1, min(1, tl));
+  ldv(vc1, min(1, tl));
+  sm(kc0, sa, 0);
+  ldk(kc0, min(2, tl));
+  wts(sa, pa, 0);
+  sm(kc1, sb, min(1, tl));
+  ldk(kc1, min(3, tl));
+  int t = 0;
+  // top of the loop: pa = P(t), sb = Sᵀ(t+1), kc0 = K(t+2), kc1 = K(t+3),
+  // vc0 = V(t), vc1 = V(t+1)
+  for (; t + 5 < nt; t += 2) {
+    mma_pv<T, D>(oacc, vc0, pa);
+    ldv(vc0, t + 2);
+    sm(kc0, sa, t + 2);
+    ldk(kc0, t + 4);
+    wts(sb, pb, t + 1);
+    interleave_tile();
+    mma_pv<T, D>(oacc, vc1, pb);
+    ldv(vc1, t + 3);
+    sm(kc1, sb, t + 3);
+    ldk(kc1, t + 5);
+    wts(sa, pa, t + 2);
+    interleave_tile();
+  }
+  const int r = nt - t;  // 1 to 5 tiles left
+  mma_pv<T, D>(oacc, vc0, pa);
+  if (r >= 2) {
+    if (r >= 3) {
+      ldv(vc0, t + 2);
+      sm(kc0, sa, t + 2);
+      if (r >= 5) ldk(kc0, t + 4);
+    }
+    wts(sb, pb, t + 1);
+    mma_pv<T, D>(oacc, vc1, pb);
+    if (r >= 3) {
+      if (r >= 4) {
+        ldv(vc1, t + 3);
+        sm(kc1, sb, t + 3);
+      }
+      wts(sa, pa, t + 2);
+      mma_pv<T, D>(oacc, vc0, pa);
+      if (r >= 4) {
+        if (r >= 5) {
+          ldv(vc0, t + 4);
+          sm(kc0, sa, t + 4);
+        }
+        wts(sb, pb, t + 3);
+        mma_pv<T, D>(oacc, vc1, pb);
+        if (r >= 5) {
+          wts(sa, pa, t + 4);
+          mma_pv<T, D>(oacc, vc0, pa);
+        }
+      }
+    }
+  }
+}
+
+// The per-block first-order pass of one 64-row query tile. `cl` is a 64 x 64
+// LDS array for the centroid logits (raw q·k̄, [block][query row]). The fast
+// kernel shifts every exponent by the Cauchy–Schwarz bound of the logits, as
+// the hybrid's fast kernel does; the careful kernel (a tile whose denominator
+// underflowed) first finds the largest exponent the tile actually uses: the
+// exact logits of its selected blocks and the centroid logits of the others.
+template <typename T, int D, bool CAREFUL, int SPB, typename Before, typename After>
+__device__ __forceinline__ void pb1_tile(const FwdArgs& a, long item, FwdShared<T, D>& sh,
+                                         typename Regs<T, D>::Xo& xo, float (*cl)[kSub],
+                                         const Before& before_sweep, const After& after_sweep) {
+  using G = Geo<T, D>;
+  constexpr int NC = G::NC, DT = G::DT, ESZ = G::ESZ, KW = G::KW;
+  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  constexpr int spb = SPB;
+  const int half = (int)(item % spb);
+  const long rest = item / spb;
+  const int i = (int)(rest % a.n);
+  const long bh = rest / a.n;
+  const int r0 = i * a.blk + half * kSub;
+  if (r0 >= a.L) {
+    after_sweep();
+    return;
+  }
+  const int nsel = a.topk;
+  const int32_t* myidx = a.idx + (bh * a.n + i) * (long)a.topk;
+  auto block_at = [&](int s) { return min(max(myidx[s], 0), a.n - 1); };
+  {
+    const int nw = (a.n + 31) >> 5;
+    for (int x = tid; x < nw; x += 128) sh.selmask[x] = 0u;
+    __syncthreads();
+    for (int s = tid; s < nsel; s += 128) {
+      const int j = block_at(s);
+      atomicOr(&sh.selmask[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+  }
+  auto selected = [&](int j) { return ((sh.selmask[j >> 5] >> (j & 31)) & 1u) != 0u; };
+
+  typename Regs<T, D>::Q qr;
+  typename Regs<T, D>::Acc oacc;
+  float m[2], l[2] = {0.f, 0.f}, asum[2] = {0.f, 0.f};
+  const float cs = a.cs;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int row = r0 + 32 * qt + l32;
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int d0 = 2 * KW * c + KW * h;
+      qr[qt][c] = row < a.L ? *(const uint4*)(a.q + (((size_t)bh * a.L + row) * D + d0) * ESZ)
+                            : make_uint4(0, 0, 0, 0);
+    }
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) oacc[dt][0] = oacc[dt][1] = f32x16{};
+
+  const size_t head_sub = (size_t)bh * a.n * spb;
+  const size_t head_ct = (size_t)bh * a.nct;
+  const bool ragged = a.n_last < a.blk;
+  const int nsub_last = (a.n_last + kSub - 1) / kSub;
+  const int g_last = (a.n - 1) * spb;  // first sub-tile of the last block
+  // Sᵀ start for global sub-tile g: −inf at keys past the end of the sequence
+  auto init_g = [&](int g) {
+    f32x16 v = f32x16{};
+    if (ragged && g >= g_last) {
+      const int nvalid = a.n_last - kSub * (g - g_last) - 32 * w;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = vkey(r, h) >= nvalid ? kNegInf : 0.0f;
+    }
+    return v;
+  };
+
+  if constexpr (!CAREFUL) {
+    float qn2[2] = {0.f, 0.f};
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) qn2[qt] = Op<T>::dot(qr[qt][c], qr[qt][c], qn2[qt]);
+    float km = 0.f;
+    for (int c = lane; c < a.nch; c += kWave) km = fmaxf(km, a.kmax2[bh * a.nch + c]);
+    km = wave_max(km);
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      const float q2 = qn2[qt] + __shfl_xor(qn2[qt], 32);
+      m[qt] = cs * sqrtf(q2 * km) - kHeadroom;
+    }
+  } else {
+    float mx[2] = {kNegInf, kNegInf};
+    typename Regs<T, D>::K kc;
+    f32x16 sx[2];
+    for (int s = 0; s < nsel; ++s) {
+      const int j = block_at(s);
+      const int nsub = (ragged && j == a.n - 1) ? nsub_last : spb;
+      for (int st = 0; st < nsub; ++st) {
+        const int g = j * spb + st;
+        load_k<T, D>(a.kp + (head_sub + g) * G::SUB_BYTES, w, lane, kc);
+        mma_s<T, D>(qr, kc, sx, init_g(g));
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx[qt] = fmaxf(mx[qt], sx[qt][r]);
+      }
+    }
+    for (int ct = 0; ct < a.nct; ++ct) {
+      load_k<T, D>(a.kbp + (head_ct + ct) * G::SUB_BYTES, w, lane, kc);
+      mma_s<T, D>(qr, kc, sx);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int j = kSub * ct + 32 * w + vkey(r, h);
+        if (j < a.n && !selected(j)) {
+          mx[0] = fmaxf(mx[0], sx[0][r]);
+          mx[1] = fmaxf(mx[1], sx[1][r]);
+        }
+      }
+    }
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      mx[qt] = fmaxf(mx[qt], __shfl_xor(mx[qt], 32));
+      if (h == 0) sh.xstat[w][0][qt][l32] = mx[qt];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) m[qt] = fmaxf(mx[qt], sh.xstat[1 - w][0][qt][l32]) * cs;
+    __syncthreads();
+  }
+
+  before_sweep();
+  for (int ct = 0; ct < a.nct; ++ct) {
+    const int j0 = kSub * ct, j1 = min(j0 + kSub, a.n);
+    {
+      typename Regs<T, D>::K kc;
+      f32x16 sx[2];
+      load_k<T, D>(a.kbp + (head_ct + ct) * G::SUB_BYTES, w, lane, kc);
+      mma_s<T, D>(qr, kc, sx);
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) cl[32 * w + vkey(r, h)][32 * qt + l32] = sx[qt][r];
+    }
+    __syncthreads();
+    const int g0 = j0 * spb;
+    const int nt = (ragged && j1 == a.n) ? g_last + nsub_last - g0 : (j1 - j0) * spb;
+    auto off = [&](int t) -> size_t { return (head_sub + g0 + t) * G::SUB_BYTES; };
+    auto init = [&](int t) { return init_g(g0 + t); };
+    auto wts = [&](const f32x16 (&sx)[2], typename Regs<T, D>::P& px, int t) {
+      const int g = g0 + t;
+      const int j = g / spb;
+      if (selected(j)) {
+        weights_full<T, D>(sx, m, l, px, cs);
+        return;
+      }
+      float a1[2], b1[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const float c = cl[j - j0][32 * qt + l32];
+        const float al = __builtin_amdgcn_exp2f(fmaf(c, cs, -m[qt]));
+        a1[qt] = al * a.scale;
+        b1[qt] = fmaf(-a1[qt], c, al);
+      }
+      if (ragged && g >= g_last)
+        weights_linear<T, D, true>(sx, a1, b1, l, px);
+      else
+        weights_linear<T, D, false>(sx, a1, b1, l, px);
+    };
+    pipelined_w<T, D>(nt, a.kp, a.vp, off, init, wts, qr, oacc, w, lane);
+    __syncthreads();  // every wavefront is done with this tile's logits
+  }
+  after_sweep();
+
+  if (w == 0)
+    epilogue<T, D, CAREFUL, 0>(a, oacc, m, l, asum, qr, sh, xo, false, bh, r0, lane, item);
+  else
+    epilogue<T, D, CAREFUL, 1>(a, oacc, m, l, asum, qr, sh, xo, false, bh, r0, lane, item);
+}
+
 }  // namespace
 
 // One workgroup per query tile, taken in order: consecutive workgroups work on
@@ -876,6 +1166,50 @@ __global__ __launch_bounds__(128, 1) void k_pisa_fwd_careful(FwdArgs a) {
   }
 }
 
+// Per-block first-order variant: one workgroup per query tile, in the same
+// generations as k_pisa_fwd (every tile sweeps all key blocks in ascending
+// order, so lining the sweeps up lets one XCD's L2 serve each K/V tile to many
+// of them).
+template <typename T, int D, int SPB>
+__global__ __launch_bounds__(128, 1) void k_pisa_pb1(FwdArgs a) {
+  __shared__ FwdShared<T, D> sh;
+  __shared__ typename Regs<T, D>::Xo xo;
+  __shared__ float cl[kSub][kSub];
+  const long item = blockIdx.x;
+  const long g = item / a.nwg;
+  auto wait = [&]() {
+    if (g > 0) {
+      if (threadIdx.x == 0) {
+        const int target = (int)(g * a.nwg);
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target &&
+               __builtin_amdgcn_s_memrealtime() - t0 < (uint64_t)a.sync_ticks)
+          __builtin_amdgcn_s_sleep(2);
+      }
+      __syncthreads();
+    }
+  };
+  auto done = [&]() {
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(a.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  pb1_tile<T, D, false, SPB>(a, item, sh, xo, cl, wait, done);
+}
+
+// The query tiles whose denominator underflowed under the fast kernel's shift,
+// again with the largest exponent each tile uses as its shift.
+template <typename T, int D, int SPB>
+__global__ __launch_bounds__(128, 1) void k_pisa_pb1_careful(FwdArgs a) {
+  __shared__ FwdShared<T, D> sh;
+  __shared__ typename Regs<T, D>::Xo xo;
+  __shared__ float cl[kSub][kSub];
+  const int count = *(volatile int*)a.redo;
+  for (int e = blockIdx.x; e < count; e += gridDim.x) {
+    const long item = a.redo[1 + e];
+    __syncthreads();
+    pb1_tile<T, D, true, SPB>(a, item, sh, xo, cl, [] {}, [] {});
+  }
+}
+
 __global__ void k_zero_counters(int* redo, int* sync) {
   *redo = 0;
   *sync = 0;
@@ -889,6 +1223,14 @@ static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <typename T, int D, int SPB>
+static hipError_t launch_pb1_t(const FwdArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_counters, dim3(1), dim3(1), 0, s, a.redo, a.sync);
+  hipLaunchKernelGGL((k_pisa_pb1<T, D, SPB>), dim3((unsigned)a.total), dim3(128), 0, s, a);
+  hipLaunchKernelGGL((k_pisa_pb1_careful<T, D, SPB>), dim3(256), dim3(128), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int D>
 static hipError_t launch_fwd_b(FwdArgs a, hipStream_t s) {
   int dev = 0, cus = 0;
@@ -897,6 +1239,8 @@ static hipError_t launch_fwd_b(FwdArgs a, hipStream_t s) {
   if (e != hipSuccess) return e;
   a.nwg = 2L * cus < a.total ? 2L * cus : a.total;  // two resident 2-wave workgroups per CU
   const bool dense = a.idx == nullptr;
+  if (a.per_block && !dense)
+    return a.blk == 64 ? launch_pb1_t<T, D, 1>(a, s) : launch_pb1_t<T, D, 2>(a, s);
   if (a.blk == 64)
     return dense ? launch_fwd_t<T, D, 1, true>(a, s) : launch_fwd_t<T, D, 1, false>(a, s);
   return dense ? launch_fwd_t<T, D, 2, true>(a, s) : launch_fwd_t<T, D, 2, false>(a, s);

@@ -143,7 +143,8 @@ pisa::FwdArgs fwd_args(const pisa_shape_t* s, const pisa::WsLayout& w, const voi
   a.nct = w.nct;
   a.cs = (float)(scale * 1.4426950408889634);
   a.scale = (float)scale;
-  a.first_order = first_order;
+  a.first_order = first_order == 1;
+  a.per_block = first_order == 2;
   a.tail = tail;
   return a;
 }
@@ -220,7 +221,7 @@ PISA_API pisa_status_t pisa_attn_fwd(const pisa_shape_t* shape, const void* q,
   if (rc != PISA_OK) return rc;
   if (!tensor_ok(q) || !tensor_ok(o)) return PISA_EINVAL;
   if (!(scale > 0.0) || !isfinite(scale)) return PISA_EINVAL;
-  if (first_order != 0 && first_order != 1) return PISA_EINVAL;
+  if (first_order < 0 || first_order > 2) return PISA_EINVAL;
   if (topk < 1 || topk > w.n) return PISA_EINVAL;
   if (idx == nullptr || !aligned(idx, 4)) return PISA_EINVAL;
   if ((rc = check_stats(st, w, false)) != PISA_OK) return rc;

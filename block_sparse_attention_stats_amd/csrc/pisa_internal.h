@@ -61,6 +61,7 @@ struct FwdArgs {
   float cs;     // scale * log2(e)
   float scale;
   int first_order, tail;
+  int per_block;  // per-block first-order variant (first_order is then 0)
 };
 
 enum StatsMode { kStatsFull = 0, kStatsMnorm = 1, kStatsPackOnly = 2 };

@@ -110,7 +110,13 @@ pisa_status_t pisa_select(const pisa_shape_t *shape, const pisa_stats_t *st, dou
  * Algorithm" N_t equation and "Hardware Implementation" phases 1-3).
  * first_order = 1: hybrid variant (zeroth order plus global first-order
  * correction, the paper version); 0: zeroth-order-only variant (README,
- * "Kernel variants"). idx [B,H,n,topk] int32, each row ascending without
+ * "Kernel variants"); 2: per-block first-order variant, every unselected
+ * block with its own first-order term alpha_tj * scale * q_t H_j (the
+ * distinct per-block terms that the gist's "Core Algorithm" replaces by the
+ * global mean H-bar; the first-order variant of the atlas summary's results),
+ * evaluated over the block's keys in one sweep over all key blocks, so it
+ * costs about as much as dense attention. Any other value: PISA_EINVAL.
+ * idx [B,H,n,topk] int32, each row ascending without
  * repeats, entries in [0, n) (any selection is accepted, e.g. one computed
  * elsewhere). Keys and values are read from the workspace copies written by
  * pisa_block_stats for the same q, k, v. o [B,H,L,D] receives the output in

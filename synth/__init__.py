@@ -44,7 +44,7 @@ class Workload:
     block: int
     density: float
     dtype: str  # "f32" or "bf16"
-    variant: str = "hyd"  # "hyd" (zeroth + global first order) or "0th"
+    variant: str = "hyd"  # "hyd" (zeroth + global first order), "0th", or "pb1" (per-block first order)
     sink_idx: int | None = None  # None, 0 or -1
     cov_weight: float = 0.0  # weight of the covariance-norm term in routing
     seed: int = 0

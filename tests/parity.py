@@ -75,11 +75,11 @@ def run_gpu(w: synth.Workload, q, k, v, oracle_idx=None):
     topk = bsa.topk_from_density(w.density, n)
     st = bsa.block_stats(q, k, v, w.block, want_mnorm=w.cov_weight > 0)
     idx = bsa.select(st, topk, s, w.cov_weight, w.sink_idx)
-    o = bsa.attn_fwd(q, st, idx, s, w.variant == "hyd")
+    o = bsa.attn_fwd(q, st, idx, s, w.variant)
     o_or = None
     if oracle_idx is not None:
         oi = torch.from_numpy(oracle_idx.astype(np.int32)).to(q.device)
-        o_or = bsa.attn_fwd(q, st, oi, s, w.variant == "hyd")
+        o_or = bsa.attn_fwd(q, st, oi, s, w.variant)
     torch.cuda.synchronize()
     return st, idx, o, o_or
 

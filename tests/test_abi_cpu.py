@@ -100,7 +100,7 @@ def test_bad_arguments_rejected():
     fwd = lambda q=FAKE, o=FAKE, fo=1, idx=FAKE, k=2, scale=0.1: lib.pisa_attn_fwd(
         ctypes.byref(s), q, ctypes.byref(st), fo, idx, k, scale, o, None)
     assert fwd(q=None) == E and fwd(q=FAKE + 8) == E and fwd(o=None) == E
-    assert fwd(fo=2) == E and fwd(k=0) == E and fwd(k=17) == E and fwd(idx=None) == E
+    assert fwd(fo=3) == E and fwd(fo=-1) == E and fwd(k=0) == E and fwd(k=17) == E and fwd(idx=None) == E
     assert fwd(scale=-1.0) == E
     assert lib.pisa_block_stats(ctypes.byref(s), FAKE, None, FAKE, ctypes.byref(st), None) == E
     assert lib.pisa_block_stats(ctypes.byref(s), FAKE, FAKE, FAKE, None, None) == E

@@ -45,6 +45,23 @@ EDGES = [
 ]
 
 
+# per-block first-order variant: ragged tails, both block sizes and dtypes,
+# a sink, covariance routing, a single block and one unselected block
+PB1 = [
+    W("pb1_bf16_ragged", 1, 3, 1000, 128, 64, 0.25, "bf16", "pb1", None, 0.0, seed=51),
+    W("pb1_bf16_blk128_short_last", 1, 2, 1050, 128, 128, 0.3, "bf16", "pb1", -1, 0.0, seed=52),
+    W("pb1_bf16_d64_sink0", 1, 2, 900, 64, 64, 0.25, "bf16", "pb1", 0, 0.0, seed=53),
+    W("pb1_f32_d128", 1, 2, 700, 128, 64, 0.3, "f32", "pb1", -1, 0.0, seed=54),
+    W("pb1_f32_blk128_d64", 1, 1, 800, 64, 128, 0.5, "f32", "pb1", None, 0.0, seed=55),
+    W("pb1_bf16_cov", 1, 2, 1200, 128, 64, 0.15, "bf16", "pb1", 0, 0.1, seed=56),
+    W("pb1_bf16_many_tiles", 1, 2, 9450, 128, 64, 0.125, "bf16", "pb1", None, 0.0, seed=57),
+    W("pb1_edge_single_block", 1, 2, 40, 128, 64, 0.5, "bf16", "pb1", None, 0.0, seed=58),
+    W("pb1_edge_last_block_one_token", 1, 2, 65, 128, 64, 0.5, "bf16", "pb1", -1, 0.0, seed=59),
+    W("pb1_edge_topk_n_minus_1", 1, 2, 500, 128, 64, 0.99, "bf16", "pb1", 0, 0.0, seed=60),
+    W("pb1_edge_density_one", 1, 2, 600, 128, 64, 1.0, "bf16", "pb1", None, 0.0, seed=61),
+]
+
+
 @pytest.fixture(autouse=True)
 def _need_gpu():
     if not torch.cuda.is_available():
@@ -59,6 +76,32 @@ def test_small_full_parity(w):
 @pytest.mark.parametrize("w", EDGES, ids=lambda w: w.name)
 def test_edge_cases(w):
     check_workload(w)
+
+
+@pytest.mark.parametrize("w", PB1, ids=lambda w: w.name)
+def test_per_block_first_order_parity(w):
+    check_workload(w)
+
+
+def test_per_block_first_order_wan_sampled():
+    """The per-block first-order variant at the full Wan shape (all heads on the
+    GPU), compared on sampled query blocks of two heads."""
+    w = synth.WAN.replace(variant="pb1", name="wan_bf16_pb1")
+    check_workload(w, heads=[(0, 3), (0, 38)], qblock_sample=6)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_per_block_first_order_careful_kernel(dtype):
+    """The loose-bound input of the hybrid's careful-kernel test, per-block
+    first-order variant: every query tile goes to its careful kernel, which
+    shifts by the largest exponent the tile uses."""
+    w = W(f"pb1_loose_bound_{dtype}", 1, 2, 700, 128, 64, 0.25, dtype, "pb1", None, 0.0, seed=42)
+    q, k, v = synth.make_qkv(w)
+    q[..., 0] = 0
+    k[:, :, 130, :] = 0
+    k[:, :, 130, 0] = 3.0e4
+    res = check_workload(w, qkv=(q, k, v))
+    assert redo_count(res["stats"], w) == w.B * w.H * w.n_blocks
 
 
 def test_tiny_config_full():
