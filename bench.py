@@ -57,11 +57,14 @@ def fused_traffic(workload: str):
     return 1024.0 * (t["fetch_kib"] * t["fetch_scale"] + t["write_kib"] * t["write_scale"])
 
 
-def flops_from_idx(idx: np.ndarray, L: int, D: int, block: int, first_order: bool) -> dict:
+def flops_from_idx(idx: np.ndarray, L: int, D: int, block: int, first_order: bool,
+                   per_block: bool = False) -> dict:
     """Credited FLOPs of one fused call: 4·D per exact (query, key) pair, 4·D
     per (query, unselected block) pair, 2·D² per query row of a query block
-    with unselected blocks (hybrid only). Centroid logits of selected blocks,
-    which the kernel computes and masks, are not credited."""
+    with unselected blocks (hybrid only), or 2·D² per (query, unselected block)
+    pair (per-block first-order variant: q_t H_j for every such block). Centroid
+    logits of selected blocks, which the kernel computes and masks, are not
+    credited."""
     B, H, n, k = idx.shape
     n_last = L - (n - 1) * block
     nq = np.full(n, block, dtype=np.float64)
@@ -71,6 +74,8 @@ def flops_from_idx(idx: np.ndarray, L: int, D: int, block: int, first_order: boo
     exact = float((nq * 4.0 * D * exact_keys).sum())
     tail = float((nq * 4.0 * D * (n - k)).sum()) * B * H
     corr = float(2.0 * D * D * nq.sum() * B * H) if (first_order and k < n) else 0.0
+    if per_block:
+        corr = float(2.0 * D * D * nq.sum() * (n - k) * B * H)
     return dict(exact=exact, tail=tail, corr=corr, total=exact + tail + corr)
 
 
@@ -189,6 +194,9 @@ def main():
     ap.add_argument("--workload", default="wan_bf16")
     ap.add_argument("--dense-reps", type=int, default=2)
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--pb1-reps", type=int, default=2,
+                    help="calls of the per-block first-order variant timed on the same selection")
+    ap.add_argument("--no-pb1", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--sweep", action="store_true",
@@ -299,6 +307,27 @@ def main():
         print(f"[bench] dense {dms:.2f} ms, {dense['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         del od, ws
 
+    pb1 = None
+    if not args.no_pb1:
+        op = torch.empty_like(qd)
+        bsa.attn_fwd(qd, st, idx, s, "pb1", out=op)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.pb1_reps):
+            bsa.attn_fwd(qd, st, idx, s, "pb1", out=op)
+        e1.record()
+        torch.cuda.synchronize()
+        pms = e0.elapsed_time(e1) / args.pb1_reps
+        fp = flops_from_idx(idx.cpu().numpy(), w.L, w.D, w.block, False, per_block=True)
+        pb1 = {"kernel": "k_pisa_pb1", "ms": pms, "flops": fp["total"],
+               "tflops": fp["total"] / (pms * 1e-3) / 1e12,
+               "mfma_frac": fp["total"] / (pms * 1e-3) / 1e12 / peak,
+               "ms_vs_hyd_fused": pms / ms["attn_fwd"],
+               "speedup_vs_dense": (dense["ms"] / pms) if dense else None}
+        print(f"[bench] pb1 {pms:.2f} ms, {pb1['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del op
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -330,6 +359,7 @@ def main():
                      "unit": "TFLOP/s", "frac": fused_tflops / peak,
                      "traffic": fused_traffic(w.name), "traffic_unit": "bytes per launch"},
         "dense": dense,
+        "pb1": pb1,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -234,7 +234,7 @@ __device__ __forceinline__ float acc_read(float x) {
   return y;
 }
 
-template <int D, bool LAG>
+template <int D, bool LAG, typename Wop>
 __device__ __forceinline__ void xstep(typename Regs<bf16, D>::Acc& oacc,
                                       typename Regs<bf16, D>::V& vc,
                                       const typename Regs<bf16, D>::P& pc,
@@ -242,7 +242,7 @@ __device__ __forceinline__ void xstep(typename Regs<bf16, D>::Acc& oacc,
                                       const typename Regs<bf16, D>::Q& qr, f32x16 (&sx)[2],
                                       const f32x16& init, const f32x16 (&sy)[2],
                                       typename Regs<bf16, D>::P& py, float (&acc)[2],
-                                      const float (&m)[2], float cs, const uint8_t* vnext,
+                                      const Wop& wop, const uint8_t* vnext,
                                       const uint8_t* knext, int w, int lane) {
   using G = Geo<bf16, D>;
   typedef bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -284,7 +284,7 @@ __device__ __forceinline__ void xstep(typename Regs<bf16, D>::Acc& oacc,
     for (int u = 0; u < EPM; ++u) {
       const int ea = mi * EPM + u, eb = ea - LG, ec = ea - 2 * LG;
       if (ea < 32) xs[ea] = acc_read(sy[ea >> 4][ea & 15]);
-      if (eb >= 0 && eb < 32) ps[eb] = __builtin_amdgcn_exp2f(fmaf(xs[eb], cs, -m[eb >> 4]));
+      if (eb >= 0 && eb < 32) ps[eb] = wop(xs[eb], eb >> 4);
       if (ec >= 0 && ec < 32 && (ec & 1)) {
         const int qt = ec >> 4, r = ec & 15;
         const bf16x2 pr = {(bf16)ps[ec - 1], (bf16)ps[ec]};
@@ -377,6 +377,7 @@ __device__ __forceinline__ void pipelined(int nt, const uint8_t* kbase, const ui
   auto wts = [&](const f32x16 (&sx)[2], typename Regs<T, D>::P& px) {
     weights_full<T, D>(sx, m, acc, px, cs);
   };
+  auto wexp = [&](float x, int qt) { return __builtin_amdgcn_exp2f(fmaf(x, cs, -m[qt])); };
   typename Regs<T, D>::K kc0, kc1;
   typename Regs<T, D>::V vc0, vc1;
   f32x16 sa[2], sb[2];
@@ -408,9 +409,9 @@ __device__ __forceinline__ void pipelined(int nt, const uint8_t* kbase, const ui
   // vc0 = V(t), vc1 = V(t+1) (each where the tile exists)
   for (; t + 5 < nt; t += 2) {
     if constexpr (sizeof(T) == 2) {
-      xstep<D, LAG>(oacc, vc0, pa, kc0, qr, sa, init_loop(t + 2), sb, pb, acc, m, cs, vbase + off(t + 2),
+      xstep<D, LAG>(oacc, vc0, pa, kc0, qr, sa, init_loop(t + 2), sb, pb, acc, wexp, vbase + off(t + 2),
                kbase + off(t + 4), w, lane);  // PV(t), S(t+2), P(t+1)
-      xstep<D, LAG>(oacc, vc1, pb, kc1, qr, sb, init_loop(t + 3), sa, pa, acc, m, cs, vbase + off(t + 3),
+      xstep<D, LAG>(oacc, vc1, pb, kc1, qr, sb, init_loop(t + 3), sa, pa, acc, wexp, vbase + off(t + 3),
                kbase + off(t + 5), w, lane);  // PV(t+1), S(t+3), P(t+2)
     } else {
       mma_pv<T, D>(oacc, vc0, pa);  // PV(t)
@@ -846,13 +847,17 @@ __device__ __forceinline__ void weights_linear(const f32x16 (&sacc)[2], const fl
   }
 }
 
-// Software-pipelined sweep over nt sub-tiles with per-tile weights wts(Sᵀ, P, t)
-// (same schedule as the generic path of `pipelined`: PV(t) and Sᵀ(t+2) on the
-// MFMA pipe while the VALU forms P(t+1); K and V double-buffered two tiles
-// ahead; loads past the end clamped to the last tile).
-template <typename T, int D, typename Off, typename Init, typename Wts>
+// Software-pipelined sweep over nt sub-tiles with per-tile weights (same
+// schedule as `pipelined`: PV(t) and Sᵀ(t+2) on the MFMA pipe while the VALU
+// forms P(t+1); K and V double-buffered two tiles ahead; loads past the end
+// clamped to the last tile). wts(Sᵀ, P, t) forms tile t's weights in the
+// prologue and the last tiles; in the main loop, which never reaches the last
+// two tiles, bf16 takes the written-out xstep with P = fma(Sᵀ, A, B),
+// exponentiated where coef(t, A, B) returns true, and row sums into acc.
+template <typename T, int D, typename Off, typename Init, typename Wts, typename Coef>
 __device__ __forceinline__ void pipelined_w(int nt, const uint8_t* kbase, const uint8_t* vbase,
                                             const Off& off, const Init& init, const Wts& wts,
+                                            const Coef& coef, float (&acc)[2],
                                             const typename Regs<T, D>::Q& qr,
                                             typename Regs<T, D>::Acc& oacc, int w, int lane) {
   if (nt <= 0) return;
@@ -879,18 +884,36 @@ __device__ __forceinline__ void pipelined_w(int nt, const uint8_t* kbase, const 
   // top of the loop: pa = P(t), sb = Sᵀ(t+1), kc0 = K(t+2), kc1 = K(t+3),
   // vc0 = V(t), vc1 = V(t+1)
   for (; t + 5 < nt; t += 2) {
-    mma_pv<T, D>(oacc, vc0, pa);
-    ldv(vc0, t + 2);
-    sm(kc0, sa, t + 2);
-    ldk(kc0, t + 4);
-    wts(sb, pb, t + 1);
-    interleave_tile();
-    mma_pv<T, D>(oacc, vc1, pb);
-    ldv(vc1, t + 3);
-    sm(kc1, sb, t + 3);
-    ldk(kc1, t + 5);
-    wts(sa, pa, t + 2);
-    interleave_tile();
+    if constexpr (sizeof(T) == 2) {
+      float A1[2], B1[2], A2[2], B2[2];
+      const bool e1 = coef(t + 1, A1, B1);
+      const bool e2 = coef(t + 2, A2, B2);
+      auto w1 = [&](float x, int qt) {
+        const float y = fmaf(x, A1[qt], B1[qt]);
+        return e1 ? __builtin_amdgcn_exp2f(y) : y;
+      };
+      auto w2 = [&](float x, int qt) {
+        const float y = fmaf(x, A2[qt], B2[qt]);
+        return e2 ? __builtin_amdgcn_exp2f(y) : y;
+      };
+      xstep<D, true>(oacc, vc0, pa, kc0, qr, sa, f32x16{}, sb, pb, acc, w1, vbase + off(t + 2),
+                     kbase + off(t + 4), w, lane);  // PV(t), Sᵀ(t+2), P(t+1)
+      xstep<D, true>(oacc, vc1, pb, kc1, qr, sb, f32x16{}, sa, pa, acc, w2, vbase + off(t + 3),
+                     kbase + off(t + 5), w, lane);  // PV(t+1), Sᵀ(t+3), P(t+2)
+    } else {
+      mma_pv<T, D>(oacc, vc0, pa);
+      ldv(vc0, t + 2);
+      sm(kc0, sa, t + 2);
+      ldk(kc0, t + 4);
+      wts(sb, pb, t + 1);
+      interleave_tile();
+      mma_pv<T, D>(oacc, vc1, pb);
+      ldv(vc1, t + 3);
+      sm(kc1, sb, t + 3);
+      ldk(kc1, t + 5);
+      wts(sa, pa, t + 2);
+      interleave_tile();
+    }
   }
   const int r = nt - t;  // 1 to 5 tiles left
   mma_pv<T, D>(oacc, vc0, pa);
@@ -1089,7 +1112,28 @@ __device__ __forceinline__ void pb1_tile(const FwdArgs& a, long item, FwdShared<
       else
         weights_linear<T, D, false>(sx, a1, b1, l, px);
     };
-    pipelined_w<T, D>(nt, a.kp, a.vp, off, init, wts, qr, oacc, w, lane);
+    // the same weights as fma(Sᵀ, A, B), exponentiated on selected blocks
+    // (tiles of the main loop are never the ragged last ones)
+    auto coef = [&](int t, float (&A)[2], float (&B)[2]) {
+      const int j = (g0 + t) / spb;
+      if (selected(j)) {
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          A[qt] = cs;
+          B[qt] = -m[qt];
+        }
+        return true;
+      }
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        const float c = cl[j - j0][32 * qt + l32];
+        const float al = __builtin_amdgcn_exp2f(fmaf(c, cs, -m[qt]));
+        A[qt] = al * a.scale;
+        B[qt] = fmaf(-A[qt], c, al);
+      }
+      return false;
+    };
+    pipelined_w<T, D>(nt, a.kp, a.vp, off, init, wts, coef, l, qr, oacc, w, lane);
     __syncthreads();  // every wavefront is done with this tile's logits
   }
   after_sweep();
