@@ -42,7 +42,12 @@ class PisaError(RuntimeError):
 
 class Shape(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("L", ctypes.c_int32),
-                ("D", ctypes.c_int32), ("block", ctypes.c_int32), ("dtype", ctypes.c_int32)]
+                ("D", ctypes.c_int32), ("block", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("layout", ctypes.c_int32)]
+
+
+# q, k, v, o memory layouts (pisa.h PISA_LAYOUT_*)
+LAYOUTS = {"BHLD": 0, "BLHD": 1}
 
 
 class StatsStruct(ctypes.Structure):
@@ -116,9 +121,15 @@ def _check_qkv(*ts: torch.Tensor):
             raise ValueError("tensors must be contiguous")
 
 
-def make_shape(q: torch.Tensor, block_size: int) -> Shape:
-    B, H, L, D = q.shape
-    return Shape(B, H, L, D, block_size, _dtype_code(q))
+def make_shape(q: torch.Tensor, block_size: int, layout: str = "BHLD") -> Shape:
+    """Shape of q laid out as [B,H,L,D] ("BHLD") or [B,L,H,D] ("BLHD")."""
+    if layout not in LAYOUTS:
+        raise ValueError(f"unknown layout {layout!r}; expected one of {sorted(LAYOUTS)}")
+    if layout == "BLHD":
+        B, L, H, D = q.shape
+    else:
+        B, H, L, D = q.shape
+    return Shape(B, H, L, D, block_size, _dtype_code(q), LAYOUTS[layout])
 
 
 def num_blocks(L: int, block_size: int) -> int:
@@ -170,10 +181,13 @@ def alloc_stats(shape: Shape, device, want_mnorm: bool) -> Stats:
                  torch.empty((B, H, n), **f64) if want_mnorm else None, ws)
 
 
-def block_stats(q, k, v, block_size: int = 64, want_mnorm: bool = False, out: Stats | None = None) -> Stats:
-    """Step 1: q̄, k̄, ΣV, H̄ (and M_j when ``want_mnorm``) via pisa_block_stats."""
+def block_stats(q, k, v, block_size: int = 64, want_mnorm: bool = False, out: Stats | None = None,
+                layout: str = "BHLD") -> Stats:
+    """Step 1: q̄, k̄, ΣV, H̄ (and M_j when ``want_mnorm``) via pisa_block_stats.
+    ``layout`` is that of q, k, v (and of the output of attn_fwd with these
+    statistics); the statistics themselves are [B,H,...] either way."""
     _check_qkv(q, k, v)
-    shape = make_shape(q, block_size)
+    shape = make_shape(q, block_size, layout)
     st = out if out is not None else alloc_stats(shape, q.device, want_mnorm)
     sst = st.struct()
     _check(load_library().pisa_block_stats(ctypes.byref(shape), q.data_ptr(), k.data_ptr(),
@@ -232,10 +246,10 @@ def attn_fwd(q, st: Stats, idx: torch.Tensor, scale: float, first_order=True,
 
 
 def dense(q, k, v, scale: float | None = None, out: torch.Tensor | None = None,
-          ws: torch.Tensor | None = None) -> torch.Tensor:
+          ws: torch.Tensor | None = None, layout: str = "BHLD") -> torch.Tensor:
     """Same-device dense attention baseline, softmax(scale·QKᵀ)V."""
     _check_qkv(q, k, v)
-    shape = make_shape(q, 64)
+    shape = make_shape(q, 64, layout)
     s = 1.0 / math.sqrt(q.shape[-1]) if scale is None else scale
     lib = load_library()
     nbytes = lib.dense_workspace_bytes(ctypes.byref(shape))
@@ -251,14 +265,17 @@ def dense(q, k, v, scale: float | None = None, out: torch.Tensor | None = None,
 
 def piecewise_sparse_attention_hyd(q, k, v, density: float = 0.15, block_size: int = 64,
                                    sink_idx=None, cov_weight: float = 0.0, scale=None,
-                                   first_order: bool = True, return_idx: bool = False):
-    """PISA forward (hybrid order: zeroth order + global first-order correction)."""
+                                   first_order=True, return_idx: bool = False,
+                                   layout: str = "BHLD"):
+    """PISA forward (hybrid order: zeroth order + global first-order correction).
+    q, k, v (and the output) are [B,H,L,D], or [B,L,H,D] with layout="BLHD"."""
     _check_qkv(q, k, v)
-    B, H, L, D = q.shape
+    shape = make_shape(q, block_size, layout)
+    L, D = shape.L, shape.D
     s = 1.0 / math.sqrt(D) if scale is None else float(scale)
     n = num_blocks(L, block_size)
     topk = topk_from_density(density, n)
-    st = block_stats(q, k, v, block_size, want_mnorm=cov_weight > 0)
+    st = block_stats(q, k, v, block_size, want_mnorm=cov_weight > 0, layout=layout)
     idx = select(st, topk, s, cov_weight, sink_idx)
     o = attn_fwd(q, st, idx, s, first_order)
     return (o, idx) if return_idx else o
@@ -266,19 +283,19 @@ def piecewise_sparse_attention_hyd(q, k, v, density: float = 0.15, block_size: i
 
 def piecewise_sparse_attention_0th(q, k, v, density: float = 0.15, block_size: int = 64,
                                    sink_idx=None, cov_weight: float = 0.0, scale=None,
-                                   return_idx: bool = False):
+                                   return_idx: bool = False, layout: str = "BHLD"):
     """PISA forward, zeroth-order-only variant (no global first-order term)."""
     return piecewise_sparse_attention_hyd(q, k, v, density, block_size, sink_idx, cov_weight, scale,
-                                          first_order=False, return_idx=return_idx)
+                                          first_order=False, return_idx=return_idx, layout=layout)
 
 
 def piecewise_sparse_attention_pb1(q, k, v, density: float = 0.15, block_size: int = 64,
                                    sink_idx=None, cov_weight: float = 0.0, scale=None,
-                                   return_idx: bool = False):
+                                   return_idx: bool = False, layout: str = "BHLD"):
     """PISA forward with a first-order term per unselected block (q·H_j for each
     block instead of the global H̄); costs about as much as dense attention."""
     return piecewise_sparse_attention_hyd(q, k, v, density, block_size, sink_idx, cov_weight, scale,
-                                          first_order="pb1", return_idx=return_idx)
+                                          first_order="pb1", return_idx=return_idx, layout=layout)
 
 
 piecewise_sparse_attention = piecewise_sparse_attention_hyd

@@ -57,6 +57,11 @@ constexpr int kEarlySignalMaxCt = 24;     // centroid tiles up to which a workgr
 
 enum TileKind { kExactFull = 0, kExactRagged = 1, kCentroid = 2 };
 
+// Byte offset of token `row` of head bh in q and o (either layout).
+__device__ __forceinline__ size_t io_row(const FwdArgs& a, long bh, int row) {
+  return (size_t)(bh / a.H) * a.stride_b + (size_t)(bh % a.H) * a.stride_h + (size_t)row * a.stride_l;
+}
+
 // Register-array types of one wavefront's state.
 template <typename T, int D>
 struct Regs {
@@ -566,7 +571,7 @@ __device__ __forceinline__ void epilogue(const FwdArgs& a, typename Regs<T, D>::
         T ov[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) ov[e] = O::from_f32(oacc[dt][qt][4 * g + e] * inv);
-        uint8_t* dst = a.o + (((size_t)bh * a.L + row) * D + d) * ESZ;
+        uint8_t* dst = a.o + io_row(a, bh, row) + (size_t)d * ESZ;
         if constexpr (ESZ == 2)
           *(uint2*)dst = __builtin_bit_cast(uint2, ov);
         else
@@ -630,7 +635,7 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int d0 = 2 * KW * c + KW * h;
-      qr[qt][c] = row < a.L ? *(const uint4*)(a.q + (((size_t)bh * a.L + row) * D + d0) * ESZ)
+      qr[qt][c] = row < a.L ? *(const uint4*)(a.q + io_row(a, bh, row) + (size_t)d0 * ESZ)
                             : make_uint4(0, 0, 0, 0);
     }
     l[qt] = 0.f;
@@ -997,7 +1002,7 @@ __device__ __forceinline__ void pb1_tile(const FwdArgs& a, long item, FwdShared<
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int d0 = 2 * KW * c + KW * h;
-      qr[qt][c] = row < a.L ? *(const uint4*)(a.q + (((size_t)bh * a.L + row) * D + d0) * ESZ)
+      qr[qt][c] = row < a.L ? *(const uint4*)(a.q + io_row(a, bh, row) + (size_t)d0 * ESZ)
                             : make_uint4(0, 0, 0, 0);
     }
   }

@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256, 2) void k_block_stats(StatsArgs a) {
   } else {
     src[0] = a.k; src[1] = a.v;
   }
-  const size_t head_bytes = (size_t)a.L * G::ROW_BYTES;
+  const size_t head_off = (size_t)(bh / a.H) * a.stride_b + (size_t)(bh % a.H) * a.stride_h;
 
   // G tiles owned by this wave: rows d in tiles dt0.., columns e in tiles et0..
   const int dt0 = TW * (wv >> 1), et0 = TW * (wv & 1);
@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256, 2) void k_block_stats(StatsArgs a) {
         const int x = tid + 256 * i, row = x / CPR, cc = x % CPR;
         const int grow = r0 + row;
         if (grow < a.L)
-          pre[t][i] = *(const uint4*)(src[t] + bh * head_bytes + (size_t)grow * G::ROW_BYTES + cc * 16);
+          pre[t][i] = *(const uint4*)(src[t] + head_off + (size_t)grow * a.stride_l + cc * 16);
         else
           pre[t][i] = make_uint4(0, 0, 0, 0);
       }

@@ -21,6 +21,7 @@ pisa_status_t check_shape(const pisa_shape_t* s, pisa::WsLayout* w) {
   if (s == nullptr) return PISA_EINVAL;
   if (s->B < 1 || s->H < 1 || s->L < 1 || s->D < 1 || s->block < 1) return PISA_EINVAL;
   if (s->dtype != PISA_F32 && s->dtype != PISA_BF16) return PISA_EINVAL;
+  if (s->layout != PISA_LAYOUT_BHLD && s->layout != PISA_LAYOUT_BLHD) return PISA_EINVAL;
   if (s->D != 64 && s->D != 128) return PISA_ENOTSUP;
   if (s->block != 64 && s->block != 128) return PISA_ENOTSUP;
   const long bh = (long)s->B * s->H;
@@ -88,6 +89,19 @@ pisa_status_t hip_status(hipError_t e) {
   return PISA_EHIP;
 }
 
+// Byte strides of q, k, v, o between batches, heads and tokens.
+void io_strides(const pisa_shape_t* s, size_t* sb, size_t* sh, size_t* sl) {
+  const size_t row = (size_t)s->D * (s->dtype == PISA_BF16 ? 2 : 4);
+  *sb = row * s->H * s->L;
+  if (s->layout == PISA_LAYOUT_BLHD) {
+    *sh = row;
+    *sl = row * s->H;
+  } else {
+    *sh = row * s->L;
+    *sl = row;
+  }
+}
+
 pisa::StatsArgs stats_args(const pisa_shape_t* s, const pisa::WsLayout& w, const void* q,
                            const void* k, const void* v, const pisa_stats_t* st, void* ws) {
   pisa::StatsArgs a;
@@ -107,6 +121,8 @@ pisa::StatsArgs stats_args(const pisa_shape_t* s, const pisa::WsLayout& w, const
   a.hbt = base + w.hbt;
   a.hpart = (float*)(base + w.hpart);
   a.kmax2 = (float*)(base + w.kmax2);
+  io_strides(s, &a.stride_b, &a.stride_h, &a.stride_l);
+  a.H = s->H;
   a.L = s->L;
   a.n = w.n;
   a.blk = s->block;
@@ -146,6 +162,8 @@ pisa::FwdArgs fwd_args(const pisa_shape_t* s, const pisa::WsLayout& w, const voi
   a.first_order = first_order == 1;
   a.per_block = first_order == 2;
   a.tail = tail;
+  io_strides(s, &a.stride_b, &a.stride_h, &a.stride_l);
+  a.H = s->H;
   return a;
 }
 

@@ -30,6 +30,10 @@ struct StatsArgs {
   uint8_t *kp, *vp, *kbp, *vbp, *hbt;
   float* hpart;
   float* kmax2;
+  // byte offset of token `row` of head bh in q, k, v: (bh / H) * stride_b +
+  // (bh % H) * stride_h + row * stride_l
+  size_t stride_b, stride_h, stride_l;
+  int H;
   int L, n, blk, cb, nch, nct;
 };
 
@@ -62,6 +66,8 @@ struct FwdArgs {
   float scale;
   int first_order, tail;
   int per_block;  // per-block first-order variant (first_order is then 0)
+  size_t stride_b, stride_h, stride_l;  // q and o addressing, as in StatsArgs
+  int H;
 };
 
 enum StatsMode { kStatsFull = 0, kStatsMnorm = 1, kStatsPackOnly = 2 };

@@ -53,12 +53,23 @@ typedef enum {
 
 typedef enum { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype_t;
 
+/* Memory layout of q, k, v and o, all contiguous:
+ * PISA_LAYOUT_BHLD [B,H,L,D], the layout of the README's functions;
+ * PISA_LAYOUT_BLHD [B,L,H,D], the layout attention processors of DiT models
+ * hold q, k, v in before their head transpose (README, the diffusers
+ * processor integration), read in place without a transposed copy. Block
+ * statistics, selections and workspace copies do not depend on it. */
+#define PISA_LAYOUT_BHLD 0
+#define PISA_LAYOUT_BLHD 1
+
 /* Problem shape. Supported: D in {64, 128}, block in {64, 128}, L >= 1,
  * B*H >= 1, dtype PISA_F32 or PISA_BF16 (I/O dtype; accumulation is fp32,
- * block statistics and routing scores are fp64). */
+ * block statistics and routing scores are fp64), layout PISA_LAYOUT_BHLD or
+ * PISA_LAYOUT_BLHD (a zero-initialised shape is BHLD). */
 typedef struct {
   int32_t B, H, L, D, block;
-  int32_t dtype; /* pisa_dtype_t */
+  int32_t dtype;  /* pisa_dtype_t */
+  int32_t layout; /* PISA_LAYOUT_* */
 } pisa_shape_t;
 
 #define PISA_SINK_NONE INT32_MIN /* sink_idx values: PISA_SINK_NONE, 0, -1 */

@@ -29,8 +29,8 @@ def test_exports_every_declared_symbol():
         assert hasattr(lib, name), name
 
 
-def shape(B=1, H=2, L=1000, D=128, block=64, dtype=bsa.PISA_BF16):
-    return bsa.Shape(B, H, L, D, block, dtype)
+def shape(B=1, H=2, L=1000, D=128, block=64, dtype=bsa.PISA_BF16, layout=0):
+    return bsa.Shape(B, H, L, D, block, dtype, layout)
 
 
 def test_workspace_sizes():
@@ -47,6 +47,11 @@ def test_workspace_sizes():
     assert lib.pisa_workspace_bytes(ctypes.byref(shape(block=32))) == 0
     assert lib.pisa_workspace_bytes(ctypes.byref(shape(L=0))) == 0
     assert lib.pisa_workspace_bytes(ctypes.byref(shape(dtype=7))) == 0
+    # [B,L,H,D] inputs need the same workspace; unknown layouts are rejected
+    assert lib.pisa_workspace_bytes(ctypes.byref(shape(layout=1))) == total
+    assert lib.dense_workspace_bytes(ctypes.byref(shape(layout=1))) == dense
+    assert lib.pisa_workspace_bytes(ctypes.byref(shape(layout=2))) == 0
+    assert lib.pisa_workspace_bytes(ctypes.byref(shape(layout=-1))) == 0
     assert lib.pisa_workspace_bytes(None) == 0
 
 

@@ -104,6 +104,45 @@ def test_per_block_first_order_careful_kernel(dtype):
     assert redo_count(res["stats"], w) == w.B * w.H * w.n_blocks
 
 
+LAYOUT_CASES = [SMALL[0], SMALL[3], SMALL[4], SMALL[5], SMALL[7], PB1[0], PB1[1]]
+
+
+@pytest.mark.parametrize("w", LAYOUT_CASES, ids=lambda w: w.name)
+def test_blhd_layout_matches_bhld(w):
+    """q, k, v given as [B,L,H,D] (layout "BLHD") and read in place: the same
+    statistics, selection and output bits as the [B,H,L,D] call, whose parity
+    with the oracle the other tests check; the dense baseline likewise. The
+    first case is also compared with the oracle directly."""
+    q, k, v = synth.make_qkv(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    qt, kt, vt = (x.transpose(1, 2).contiguous() for x in (qd, kd, vd))
+    n = w.n_blocks
+    topk = bsa.topk_from_density(w.density, n)
+    runs = []
+    for (a, b, c, lay) in ((qd, kd, vd, "BHLD"), (qt, kt, vt, "BLHD")):
+        st = bsa.block_stats(a, b, c, w.block, want_mnorm=w.cov_weight > 0, layout=lay)
+        idx = bsa.select(st, topk, w.scale, w.cov_weight, w.sink_idx)
+        o = bsa.attn_fwd(a, st, idx, w.scale, w.variant)
+        od = bsa.dense(a, b, c, w.scale, layout=lay)
+        runs.append((st, idx, o, od))
+    torch.cuda.synchronize()
+    (s1, i1, o1, d1), (s2, i2, o2, d2) = runs
+    for name in ("qbar", "kbar", "vsum", "hbar"):
+        assert torch.equal(getattr(s1, name), getattr(s2, name)), name
+    assert torch.equal(i1, i2)
+    assert o2.shape == (w.B, w.L, w.H, w.D)
+    assert torch.equal(o2.transpose(1, 2), o1)
+    assert torch.equal(d2.transpose(1, 2), d1)
+    if w is LAYOUT_CASES[0]:
+        for h in range(w.H):
+            qh, kh, vh = (synth.as_f64(x[0, h]) for x in (q, k, v))
+            o_ref, idx_ref = oracle.head_forward(qh, kh, vh, block=w.block, topk=topk, scale=w.scale,
+                                                 variant=w.variant, sink_idx=w.sink_idx,
+                                                 idx=i2[0, h].cpu().numpy())
+            compare_out(o2[0, :, h].float().cpu().numpy(), o_ref, w.dtype, f"BLHD head {h}")
+
+
 def test_tiny_config_full():
     check_workload(synth.TINY)
 
