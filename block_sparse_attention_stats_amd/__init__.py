@@ -31,7 +31,8 @@ PISA_OK, PISA_EINVAL, PISA_ENOTSUP, PISA_EHIP = 0, 1, 2, 3
 PISA_F32, PISA_BF16 = 0, 1
 PISA_SINK_NONE = -(2 ** 31)
 EXPORTS = ("pisa_workspace_bytes", "pisa_block_stats", "pisa_select", "pisa_attn_fwd",
-           "dense_workspace_bytes", "dense_attn_fwd", "pisa_status_string", "pisa_last_hip_error")
+           "dense_workspace_bytes", "dense_attn_fwd", "pisa_status_string", "pisa_last_hip_error",
+           "pisa_block_stats_seg", "pisa_attn_fwd_seg", "dense_attn_fwd_seg")
 
 
 class PisaError(RuntimeError):
@@ -48,6 +49,13 @@ class Shape(ctypes.Structure):
 
 # q, k, v, o memory layouts (pisa.h PISA_LAYOUT_*)
 LAYOUTS = {"BHLD": 0, "BLHD": 1}
+
+
+class Segments(ctypes.Structure):
+    """A sequence held in two tensors: tokens [0, L0) in the usual q, k, v (o)
+    arguments, the rest in q1, k1, v1 (o1)."""
+    _fields_ = [("L0", ctypes.c_int32), ("q1", ctypes.c_void_p), ("k1", ctypes.c_void_p),
+                ("v1", ctypes.c_void_p), ("o1", ctypes.c_void_p)]
 
 
 class StatsStruct(ctypes.Structure):
@@ -69,7 +77,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                            "`python -m block_sparse_attention_stats_amd.build`")
     lib = ctypes.CDLL(path)
     P, I32, D64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_double, ctypes.c_size_t
-    SP, STP = ctypes.POINTER(Shape), ctypes.POINTER(StatsStruct)
+    SP, STP, SG = ctypes.POINTER(Shape), ctypes.POINTER(StatsStruct), ctypes.POINTER(Segments)
     sig = {
         "pisa_workspace_bytes": (SZ, [SP]),
         "dense_workspace_bytes": (SZ, [SP]),
@@ -77,6 +85,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pisa_select": (I32, [SP, STP, D64, D64, I32, I32, P, P]),
         "pisa_attn_fwd": (I32, [SP, P, STP, I32, P, I32, D64, P, P]),
         "dense_attn_fwd": (I32, [SP, P, P, P, D64, P, P, SZ, P]),
+        "pisa_block_stats_seg": (I32, [SP, P, P, P, SG, STP, P]),
+        "pisa_attn_fwd_seg": (I32, [SP, P, STP, I32, P, I32, D64, P, SG, P]),
+        "dense_attn_fwd_seg": (I32, [SP, P, P, P, SG, D64, P, P, SZ, P]),
         "pisa_status_string": (ctypes.c_char_p, [I32]),
         "pisa_last_hip_error": (ctypes.c_char_p, []),
     }
@@ -299,3 +310,104 @@ def piecewise_sparse_attention_pb1(q, k, v, density: float = 0.15, block_size: i
 
 
 piecewise_sparse_attention = piecewise_sparse_attention_hyd
+
+
+# --------------------------------------------------------------------------
+# Joint attention over a sequence held in two tensors (MMDiT text and image
+# streams), without a concatenated copy.
+
+def _joint_shape(q0: torch.Tensor, q1: torch.Tensor, block_size: int, layout: str) -> Shape:
+    shape = make_shape(q0, block_size, layout)
+    s1 = make_shape(q1, block_size, layout)
+    if (s1.B, s1.H, s1.D, s1.dtype) != (shape.B, shape.H, shape.D, shape.dtype):
+        raise ValueError("both parts must have the same batch, heads, head_dim and dtype")
+    shape.L = shape.L + s1.L
+    return shape
+
+
+def _segments(L0: int, q1, k1=None, v1=None, o1=None) -> Segments:
+    ptr = lambda t: None if t is None else t.data_ptr()
+    return Segments(L0, ptr(q1), ptr(k1), ptr(v1), ptr(o1))
+
+
+def block_stats_seg(q0, k0, v0, q1, k1, v1, block_size: int = 64, want_mnorm: bool = False,
+                    out: Stats | None = None, layout: str = "BHLD") -> Stats:
+    """Step 1 on the sequence q0 ++ q1 (and k, v likewise), via pisa_block_stats_seg."""
+    _check_qkv(q0, k0, v0)
+    _check_qkv(q1, k1, v1)
+    shape = _joint_shape(q0, q1, block_size, layout)
+    L0 = shape.L - make_shape(q1, block_size, layout).L
+    st = out if out is not None else alloc_stats(shape, q0.device, want_mnorm)
+    sst = st.struct()
+    seg = _segments(L0, q1, k1, v1)
+    _check(load_library().pisa_block_stats_seg(ctypes.byref(shape), q0.data_ptr(), k0.data_ptr(),
+                                               v0.data_ptr(), ctypes.byref(seg), ctypes.byref(sst),
+                                               _stream()), "pisa_block_stats_seg")
+    return st
+
+
+def attn_fwd_seg(q0, q1, st: Stats, idx: torch.Tensor, scale: float, first_order=True,
+                 out0: torch.Tensor | None = None, out1: torch.Tensor | None = None):
+    """Step 3 on the sequence q0 ++ q1; returns the output in two parts shaped
+    like q0 and q1."""
+    _check_qkv(q0)
+    _check_qkv(q1)
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or not idx.is_cuda:
+        raise ValueError("idx must be a contiguous int32 GPU tensor")
+    code = VARIANTS[first_order] if isinstance(first_order, str) else (1 if first_order else 0)
+    shape = st.shape
+    layout = "BLHD" if shape.layout == LAYOUTS["BLHD"] else "BHLD"
+    L0 = shape.L - make_shape(q1, shape.block, layout).L
+    o0 = out0 if out0 is not None else torch.empty_like(q0)
+    o1 = out1 if out1 is not None else torch.empty_like(q1)
+    sst = st.struct()
+    seg = _segments(L0, q1, o1=o1)
+    _check(load_library().pisa_attn_fwd_seg(ctypes.byref(shape), q0.data_ptr(), ctypes.byref(sst), code,
+                                            idx.data_ptr(), int(idx.shape[-1]), float(scale),
+                                            o0.data_ptr(), ctypes.byref(seg), _stream()),
+           "pisa_attn_fwd_seg")
+    return o0, o1
+
+
+def dense_seg(q0, k0, v0, q1, k1, v1, scale: float | None = None, layout: str = "BHLD"):
+    """Dense baseline on the sequence q0 ++ q1; output in two parts."""
+    _check_qkv(q0, k0, v0)
+    _check_qkv(q1, k1, v1)
+    shape = _joint_shape(q0, q1, 64, layout)
+    L0 = shape.L - make_shape(q1, 64, layout).L
+    s = 1.0 / math.sqrt(q0.shape[-1]) if scale is None else scale
+    lib = load_library()
+    nbytes = lib.dense_workspace_bytes(ctypes.byref(shape))
+    if nbytes == 0:
+        raise PisaError(PISA_EINVAL, "dense_workspace_bytes")
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=q0.device)
+    o0, o1 = torch.empty_like(q0), torch.empty_like(q1)
+    seg = _segments(L0, q1, k1, v1, o1)
+    _check(lib.dense_attn_fwd_seg(ctypes.byref(shape), q0.data_ptr(), k0.data_ptr(), v0.data_ptr(),
+                                  ctypes.byref(seg), float(s), o0.data_ptr(), ws.data_ptr(), ws.numel(),
+                                  _stream()), "dense_attn_fwd_seg")
+    return o0, o1
+
+
+def mmdit_joint_attention(txt_q, txt_k, txt_v, img_q, img_k, img_v, density: float = 0.15,
+                          block_size: int = 64, text_first: bool = True, variant="hyd",
+                          cov_weight: float = 0.0, scale=None, layout: str = "BHLD",
+                          return_idx: bool = False):
+    """PISA over the joint text + image sequence of an MMDiT block, with the
+    text block as the attention sink (README, "Attention sink for MMDiT"):
+    text first (FLUX) forces block 0, text last (Hunyuan-Video) block n-1.
+    Returns (o_txt, o_img), shaped like the inputs."""
+    if text_first:
+        parts, sink = ((txt_q, txt_k, txt_v), (img_q, img_k, img_v)), 0
+    else:
+        parts, sink = ((img_q, img_k, img_v), (txt_q, txt_k, txt_v)), -1
+    (q0, k0, v0), (q1, k1, v1) = parts
+    shape = _joint_shape(q0, q1, block_size, layout)
+    s = 1.0 / math.sqrt(shape.D) if scale is None else float(scale)
+    topk = topk_from_density(density, num_blocks(shape.L, block_size))
+    st = block_stats_seg(q0, k0, v0, q1, k1, v1, block_size, want_mnorm=cov_weight > 0, layout=layout)
+    idx = select(st, topk, s, cov_weight, sink)
+    o0, o1 = attn_fwd_seg(q0, q1, st, idx, s, variant)
+    o_txt, o_img = (o0, o1) if text_first else (o1, o0)
+    return (o_txt, o_img, idx) if return_idx else (o_txt, o_img)
+

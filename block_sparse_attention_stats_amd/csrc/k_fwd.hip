@@ -57,9 +57,20 @@ constexpr int kEarlySignalMaxCt = 24;     // centroid tiles up to which a workgr
 
 enum TileKind { kExactFull = 0, kExactRagged = 1, kCentroid = 2 };
 
-// Byte offset of token `row` of head bh in q and o (either layout).
-__device__ __forceinline__ size_t io_row(const FwdArgs& a, long bh, int row) {
-  return (size_t)(bh / a.H) * a.stride_b + (size_t)(bh % a.H) * a.stride_h + (size_t)row * a.stride_l;
+// Address of token `row` of head bh in q (OUT false) or o (OUT true): either
+// layout, and either part of a sequence held in two tensors.
+template <bool OUT>
+__device__ __forceinline__ auto io_row(const FwdArgs& a, long bh, int row) {
+  const long b = bh / a.H, h = bh % a.H;
+  if (row < a.L0) {
+    const size_t off = (size_t)b * a.stride_b + (size_t)h * a.stride_h + (size_t)row * a.stride_l;
+    if constexpr (OUT) return a.o + off; else return a.q + off;
+  }
+  // The second part's fields are read here, where they are used, rather than
+  // held in scalar registers through the whole kernel.
+  const volatile FwdArgs& v = a;
+  const size_t off = (size_t)b * v.stride1_b + (size_t)h * v.stride1_h + (size_t)(row - a.L0) * v.stride1_l;
+  if constexpr (OUT) return (uint8_t*)v.o1 + off; else return (const uint8_t*)v.q1 + off;
 }
 
 // Register-array types of one wavefront's state.
@@ -571,7 +582,7 @@ __device__ __forceinline__ void epilogue(const FwdArgs& a, typename Regs<T, D>::
         T ov[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) ov[e] = O::from_f32(oacc[dt][qt][4 * g + e] * inv);
-        uint8_t* dst = a.o + io_row(a, bh, row) + (size_t)d * ESZ;
+        uint8_t* dst = io_row<true>(a, bh, row) + (size_t)d * ESZ;
         if constexpr (ESZ == 2)
           *(uint2*)dst = __builtin_bit_cast(uint2, ov);
         else
@@ -635,7 +646,7 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int d0 = 2 * KW * c + KW * h;
-      qr[qt][c] = row < a.L ? *(const uint4*)(a.q + io_row(a, bh, row) + (size_t)d0 * ESZ)
+      qr[qt][c] = row < a.L ? *(const uint4*)(io_row<false>(a, bh, row) + (size_t)d0 * ESZ)
                             : make_uint4(0, 0, 0, 0);
     }
     l[qt] = 0.f;
@@ -1002,7 +1013,7 @@ __device__ __forceinline__ void pb1_tile(const FwdArgs& a, long item, FwdShared<
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       const int d0 = 2 * KW * c + KW * h;
-      qr[qt][c] = row < a.L ? *(const uint4*)(a.q + io_row(a, bh, row) + (size_t)d0 * ESZ)
+      qr[qt][c] = row < a.L ? *(const uint4*)(io_row<false>(a, bh, row) + (size_t)d0 * ESZ)
                             : make_uint4(0, 0, 0, 0);
     }
   }

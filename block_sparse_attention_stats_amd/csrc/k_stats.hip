@@ -21,7 +21,10 @@
 
 namespace pisa {
 
-template <typename T, int D, int MODE>
+// SEG: the sequence is held in two tensors (rows from L0 on in q1, k1, v1).
+// Without it the kernel never touches the second part, which keeps its state
+// out of the registers the single-tensor case needs.
+template <typename T, int D, int MODE, bool SEG>
 __global__ __launch_bounds__(256, 2) void k_block_stats(StatsArgs a) {
   using G = Geo<T, D>;
   using O = Op<T>;
@@ -46,13 +49,17 @@ __global__ __launch_bounds__(256, 2) void k_block_stats(StatsArgs a) {
   const int j0 = ch * a.cb, j1 = min(a.n, j0 + a.cb);
   const int spb = a.blk / kSub;
   const int total_sub = (j1 - j0) * spb;
-  const uint8_t* src[NT];
+  const uint8_t *src[NT], *src1[NT];  // the two segments of the sequence
   if constexpr (MODE == kStatsFull) {
     src[0] = a.q; src[1] = a.k; src[2] = a.v;
+    src1[0] = a.q1; src1[1] = a.k1; src1[2] = a.v1;
   } else {
     src[0] = a.k; src[1] = a.v;
+    src1[0] = a.k1; src1[1] = a.v1;
   }
-  const size_t head_off = (size_t)(bh / a.H) * a.stride_b + (size_t)(bh % a.H) * a.stride_h;
+  const long bat = bh / a.H, hd = bh % a.H;
+  const size_t head_off = (size_t)bat * a.stride_b + (size_t)hd * a.stride_h;
+  const size_t head_off1 = (size_t)bat * a.stride1_b + (size_t)hd * a.stride1_h;
 
   // G tiles owned by this wave: rows d in tiles dt0.., columns e in tiles et0..
   const int dt0 = TW * (wv >> 1), et0 = TW * (wv & 1);
@@ -91,17 +98,48 @@ __global__ __launch_bounds__(256, 2) void k_block_stats(StatsArgs a) {
   auto load_sub = [&](int s) {
     const int j = j0 + s / spb, st = s % spb;
     const int r0 = j * a.blk + st * kSub;
+    if constexpr (!SEG) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t)
+      for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int i = 0; i < PER; ++i) {
-        const int x = tid + 256 * i, row = x / CPR, cc = x % CPR;
-        const int grow = r0 + row;
-        if (grow < a.L)
-          pre[t][i] = *(const uint4*)(src[t] + head_off + (size_t)grow * a.stride_l + cc * 16);
-        else
-          pre[t][i] = make_uint4(0, 0, 0, 0);
+        for (int i = 0; i < PER; ++i) {
+          const int x = tid + 256 * i, row = x / CPR, cc = x % CPR;
+          const int grow = r0 + row;
+          if (grow < a.L)
+            pre[t][i] = *(const uint4*)(src[t] + head_off + (size_t)grow * a.stride_l + cc * 16);
+          else
+            pre[t][i] = make_uint4(0, 0, 0, 0);
+        }
+      return;
+    }
+    // The 64 rows lie in one part of the sequence unless they straddle L0:
+    // then one base and stride (uniform) serve every load.
+    const bool in0 = r0 + kSub <= a.L0, in1 = r0 >= a.L0;
+    if (in0 || in1) {
+      const size_t sl = in0 ? a.stride_l : a.stride1_l;
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const uint8_t* base = in0 ? src[t] + head_off + (size_t)r0 * sl
+                                  : src1[t] + head_off1 + (size_t)(r0 - a.L0) * sl;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int x = tid + 256 * i, row = x / CPR, cc = x % CPR;
+          pre[t][i] = r0 + row < a.L ? *(const uint4*)(base + (size_t)row * sl + cc * 16)
+                                     : make_uint4(0, 0, 0, 0);
+        }
       }
+    } else {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < PER; ++i) {
+          const int x = tid + 256 * i, row = x / CPR, cc = x % CPR;
+          const int grow = r0 + row;
+          const uint8_t* p = grow < a.L0 ? src[t] + head_off + (size_t)grow * a.stride_l
+                                         : src1[t] + head_off1 + (size_t)(grow - a.L0) * a.stride1_l;
+          pre[t][i] = grow < a.L ? *(const uint4*)(p + cc * 16) : make_uint4(0, 0, 0, 0);
+        }
+    }
   };
 
   if (total_sub > 0) load_sub(0);
@@ -338,16 +376,22 @@ __global__ __launch_bounds__(256) void k_hbar_reduce(StatsArgs a) {
   }
 }
 
-template <typename T, int D>
-static hipError_t launch_stats_t(int mode, const StatsArgs& a, long bh, hipStream_t s) {
+template <typename T, int D, bool SEG>
+static hipError_t launch_stats_s(int mode, const StatsArgs& a, long bh, hipStream_t s) {
   dim3 grid((unsigned)(bh * a.nch));
   if (mode == kStatsFull)
-    hipLaunchKernelGGL((k_block_stats<T, D, kStatsFull>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_block_stats<T, D, kStatsFull, SEG>), grid, dim3(256), 0, s, a);
   else if (mode == kStatsMnorm)
-    hipLaunchKernelGGL((k_block_stats<T, D, kStatsMnorm>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_block_stats<T, D, kStatsMnorm, SEG>), grid, dim3(256), 0, s, a);
   else
-    hipLaunchKernelGGL((k_block_stats<T, D, kStatsPackOnly>), grid, dim3(256), 0, s, a);
+    hipLaunchKernelGGL((k_block_stats<T, D, kStatsPackOnly, SEG>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_stats_t(int mode, const StatsArgs& a, long bh, hipStream_t s) {
+  return a.L0 < a.L ? launch_stats_s<T, D, true>(mode, a, bh, s)
+                    : launch_stats_s<T, D, false>(mode, a, bh, s);
 }
 
 hipError_t launch_block_stats(int dtype, int D, int mode, const StatsArgs& a, long bh,

@@ -89,21 +89,38 @@ pisa_status_t hip_status(hipError_t e) {
   return PISA_EHIP;
 }
 
-// Byte strides of q, k, v, o between batches, heads and tokens.
-void io_strides(const pisa_shape_t* s, size_t* sb, size_t* sh, size_t* sl) {
+// Byte strides between batches, heads and tokens of a q, k, v or o tensor
+// holding Lseg tokens of the sequence.
+void io_strides(const pisa_shape_t* s, long Lseg, size_t* sb, size_t* sh, size_t* sl) {
   const size_t row = (size_t)s->D * (s->dtype == PISA_BF16 ? 2 : 4);
-  *sb = row * s->H * s->L;
+  *sb = row * s->H * Lseg;
   if (s->layout == PISA_LAYOUT_BLHD) {
     *sh = row;
     *sl = row * s->H;
   } else {
-    *sh = row * s->L;
+    *sh = row * Lseg;
     *sl = row;
   }
 }
 
+// Tokens in the first segment of the sequence (all of them without seg).
+long seg_L0(const pisa_shape_t* s, const pisa_segments_t* seg) { return seg ? seg->L0 : s->L; }
+
+// A second segment must hold 1 .. L-1 tokens and aligned tensors for what the
+// call reads (and writes); L0 == L leaves it empty and its pointers unused.
+pisa_status_t check_seg(const pisa_shape_t* s, const pisa_segments_t* seg, bool k_v, bool q_o) {
+  if (seg == nullptr) return PISA_OK;
+  if (seg->L0 < 1 || seg->L0 > s->L) return PISA_EINVAL;
+  if (seg->L0 == s->L) return PISA_OK;
+  if (!tensor_ok(seg->q1)) return PISA_EINVAL;
+  if (k_v && (!tensor_ok(seg->k1) || !tensor_ok(seg->v1))) return PISA_EINVAL;
+  if (q_o && !tensor_ok(seg->o1)) return PISA_EINVAL;
+  return PISA_OK;
+}
+
 pisa::StatsArgs stats_args(const pisa_shape_t* s, const pisa::WsLayout& w, const void* q,
-                           const void* k, const void* v, const pisa_stats_t* st, void* ws) {
+                           const void* k, const void* v, const pisa_segments_t* seg,
+                           const pisa_stats_t* st, void* ws) {
   pisa::StatsArgs a;
   uint8_t* base = (uint8_t*)ws;
   a.q = (const uint8_t*)q;
@@ -121,7 +138,13 @@ pisa::StatsArgs stats_args(const pisa_shape_t* s, const pisa::WsLayout& w, const
   a.hbt = base + w.hbt;
   a.hpart = (float*)(base + w.hpart);
   a.kmax2 = (float*)(base + w.kmax2);
-  io_strides(s, &a.stride_b, &a.stride_h, &a.stride_l);
+  const long L0 = seg_L0(s, seg);
+  io_strides(s, L0, &a.stride_b, &a.stride_h, &a.stride_l);
+  io_strides(s, s->L - L0, &a.stride1_b, &a.stride1_h, &a.stride1_l);
+  a.q1 = (const uint8_t*)(seg ? seg->q1 : nullptr);
+  a.k1 = (const uint8_t*)(seg ? seg->k1 : nullptr);
+  a.v1 = (const uint8_t*)(seg ? seg->v1 : nullptr);
+  a.L0 = (int)L0;
   a.H = s->H;
   a.L = s->L;
   a.n = w.n;
@@ -133,8 +156,8 @@ pisa::StatsArgs stats_args(const pisa_shape_t* s, const pisa::WsLayout& w, const
 }
 
 pisa::FwdArgs fwd_args(const pisa_shape_t* s, const pisa::WsLayout& w, const void* q, void* o,
-                       void* ws, const int32_t* idx, int topk, double scale, int first_order,
-                       int tail) {
+                       const pisa_segments_t* seg, void* ws, const int32_t* idx, int topk,
+                       double scale, int first_order, int tail) {
   pisa::FwdArgs a;
   uint8_t* base = (uint8_t*)ws;
   a.q = (const uint8_t*)q;
@@ -162,7 +185,12 @@ pisa::FwdArgs fwd_args(const pisa_shape_t* s, const pisa::WsLayout& w, const voi
   a.first_order = first_order == 1;
   a.per_block = first_order == 2;
   a.tail = tail;
-  io_strides(s, &a.stride_b, &a.stride_h, &a.stride_l);
+  const long L0 = seg_L0(s, seg);
+  io_strides(s, L0, &a.stride_b, &a.stride_h, &a.stride_l);
+  io_strides(s, s->L - L0, &a.stride1_b, &a.stride1_h, &a.stride1_l);
+  a.q1 = (const uint8_t*)(seg ? seg->q1 : nullptr);
+  a.o1 = (uint8_t*)(seg ? seg->o1 : nullptr);
+  a.L0 = (int)L0;
   a.H = s->H;
   return a;
 }
@@ -179,15 +207,18 @@ PISA_API size_t dense_workspace_bytes(const pisa_shape_t* shape) {
   return check_shape(shape, &w) == PISA_OK ? w.dense_total : 0;
 }
 
-PISA_API pisa_status_t pisa_block_stats(const pisa_shape_t* shape, const void* q, const void* k,
-                                        const void* v, const pisa_stats_t* st, void* stream) {
+PISA_API pisa_status_t pisa_block_stats_seg(const pisa_shape_t* shape, const void* q,
+                                            const void* k, const void* v,
+                                            const pisa_segments_t* seg, const pisa_stats_t* st,
+                                            void* stream) {
   pisa::WsLayout w;
   pisa_status_t rc = check_shape(shape, &w);
   if (rc != PISA_OK) return rc;
   if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v)) return PISA_EINVAL;
+  if ((rc = check_seg(shape, seg, true, false)) != PISA_OK) return rc;
   if ((rc = check_stats(st, w, false)) != PISA_OK) return rc;
   hipStream_t s = (hipStream_t)stream;
-  pisa::StatsArgs a = stats_args(shape, w, q, k, v, st, st->ws);
+  pisa::StatsArgs a = stats_args(shape, w, q, k, v, seg, st, st->ws);
   if ((rc = hip_status(pisa::launch_block_stats(shape->dtype, shape->D, pisa::kStatsFull, a, w.bh, s))))
     return rc;
   if ((rc = hip_status(pisa::launch_hbar_reduce(shape->dtype, shape->D, a, w.bh, s)))) return rc;
@@ -195,6 +226,11 @@ PISA_API pisa_status_t pisa_block_stats(const pisa_shape_t* shape, const void* q
     if ((rc = hip_status(pisa::launch_block_stats(shape->dtype, shape->D, pisa::kStatsMnorm, a, w.bh, s))))
       return rc;
   return PISA_OK;
+}
+
+PISA_API pisa_status_t pisa_block_stats(const pisa_shape_t* shape, const void* q, const void* k,
+                                        const void* v, const pisa_stats_t* st, void* stream) {
+  return pisa_block_stats_seg(shape, q, k, v, nullptr, st, stream);
 }
 
 PISA_API pisa_status_t pisa_select(const pisa_shape_t* shape, const pisa_stats_t* st, double scale,
@@ -230,38 +266,53 @@ PISA_API pisa_status_t pisa_select(const pisa_shape_t* shape, const pisa_stats_t
   return hip_status(pisa::launch_topk(ta, w.bh * w.n, s));
 }
 
-PISA_API pisa_status_t pisa_attn_fwd(const pisa_shape_t* shape, const void* q,
-                                     const pisa_stats_t* st, int32_t first_order,
-                                     const int32_t* idx, int32_t topk, double scale, void* o,
-                                     void* stream) {
+PISA_API pisa_status_t pisa_attn_fwd_seg(const pisa_shape_t* shape, const void* q,
+                                         const pisa_stats_t* st, int32_t first_order,
+                                         const int32_t* idx, int32_t topk, double scale, void* o,
+                                         const pisa_segments_t* seg, void* stream) {
   pisa::WsLayout w;
   pisa_status_t rc = check_shape(shape, &w);
   if (rc != PISA_OK) return rc;
   if (!tensor_ok(q) || !tensor_ok(o)) return PISA_EINVAL;
+  if ((rc = check_seg(shape, seg, false, true)) != PISA_OK) return rc;
   if (!(scale > 0.0) || !isfinite(scale)) return PISA_EINVAL;
   if (first_order < 0 || first_order > 2) return PISA_EINVAL;
   if (topk < 1 || topk > w.n) return PISA_EINVAL;
   if (idx == nullptr || !aligned(idx, 4)) return PISA_EINVAL;
   if ((rc = check_stats(st, w, false)) != PISA_OK) return rc;
-  pisa::FwdArgs a = fwd_args(shape, w, q, o, st->ws, idx, topk, scale, first_order, 1);
+  pisa::FwdArgs a = fwd_args(shape, w, q, o, seg, st->ws, idx, topk, scale, first_order, 1);
   return hip_status(pisa::launch_fwd(shape->dtype, shape->D, a, (hipStream_t)stream));
+}
+
+PISA_API pisa_status_t pisa_attn_fwd(const pisa_shape_t* shape, const void* q,
+                                     const pisa_stats_t* st, int32_t first_order,
+                                     const int32_t* idx, int32_t topk, double scale, void* o,
+                                     void* stream) {
+  return pisa_attn_fwd_seg(shape, q, st, first_order, idx, topk, scale, o, nullptr, stream);
+}
+
+PISA_API pisa_status_t dense_attn_fwd_seg(const pisa_shape_t* shape, const void* q, const void* k,
+                                          const void* v, const pisa_segments_t* seg, double scale,
+                                          void* o, void* ws, size_t ws_bytes, void* stream) {
+  pisa::WsLayout w;
+  pisa_status_t rc = check_shape(shape, &w);
+  if (rc != PISA_OK) return rc;
+  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o)) return PISA_EINVAL;
+  if ((rc = check_seg(shape, seg, true, true)) != PISA_OK) return rc;
+  if (!(scale > 0.0) || !isfinite(scale)) return PISA_EINVAL;
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < w.dense_total) return PISA_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  pisa::StatsArgs sa = stats_args(shape, w, q, k, v, seg, nullptr, ws);
+  if ((rc = hip_status(pisa::launch_block_stats(shape->dtype, shape->D, pisa::kStatsPackOnly, sa, w.bh, s))))
+    return rc;
+  pisa::FwdArgs a = fwd_args(shape, w, q, o, seg, ws, nullptr, w.n, scale, 0, 0);
+  return hip_status(pisa::launch_fwd(shape->dtype, shape->D, a, s));
 }
 
 PISA_API pisa_status_t dense_attn_fwd(const pisa_shape_t* shape, const void* q, const void* k,
                                       const void* v, double scale, void* o, void* ws,
                                       size_t ws_bytes, void* stream) {
-  pisa::WsLayout w;
-  pisa_status_t rc = check_shape(shape, &w);
-  if (rc != PISA_OK) return rc;
-  if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v) || !tensor_ok(o)) return PISA_EINVAL;
-  if (!(scale > 0.0) || !isfinite(scale)) return PISA_EINVAL;
-  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < w.dense_total) return PISA_EINVAL;
-  hipStream_t s = (hipStream_t)stream;
-  pisa::StatsArgs sa = stats_args(shape, w, q, k, v, nullptr, ws);
-  if ((rc = hip_status(pisa::launch_block_stats(shape->dtype, shape->D, pisa::kStatsPackOnly, sa, w.bh, s))))
-    return rc;
-  pisa::FwdArgs a = fwd_args(shape, w, q, o, ws, nullptr, w.n, scale, 0, 0);
-  return hip_status(pisa::launch_fwd(shape->dtype, shape->D, a, s));
+  return dense_attn_fwd_seg(shape, q, k, v, nullptr, scale, o, ws, ws_bytes, stream);
 }
 
 PISA_API const char* pisa_status_string(pisa_status_t status) {

@@ -30,10 +30,14 @@ struct StatsArgs {
   uint8_t *kp, *vp, *kbp, *vbp, *hbt;
   float* hpart;
   float* kmax2;
-  // byte offset of token `row` of head bh in q, k, v: (bh / H) * stride_b +
-  // (bh % H) * stride_h + row * stride_l
+  // Token `row` of head bh: rows below L0 are in q, k, v at byte offset
+  // (bh / H) * stride_b + (bh % H) * stride_h + row * stride_l; rows from L0
+  // on are in q1, k1, v1, at the same form of offset with stride1_* and
+  // row - L0 (the second segment of a joint sequence; L0 = L when there is none)
   size_t stride_b, stride_h, stride_l;
-  int H;
+  const uint8_t *q1, *k1, *v1;
+  size_t stride1_b, stride1_h, stride1_l;
+  int H, L0;
   int L, n, blk, cb, nch, nct;
 };
 
@@ -67,7 +71,10 @@ struct FwdArgs {
   int first_order, tail;
   int per_block;  // per-block first-order variant (first_order is then 0)
   size_t stride_b, stride_h, stride_l;  // q and o addressing, as in StatsArgs
-  int H;
+  const uint8_t* q1;                    // second segment of q and o
+  uint8_t* o1;
+  size_t stride1_b, stride1_h, stride1_l;
+  int H, L0;
 };
 
 enum StatsMode { kStatsFull = 0, kStatsMnorm = 1, kStatsPackOnly = 2 };

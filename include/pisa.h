@@ -146,6 +146,42 @@ pisa_status_t dense_attn_fwd(const pisa_shape_t *shape, const void *q, const voi
                              const void *v, double scale, void *o, void *ws, size_t ws_bytes,
                              void *stream);
 
+/* Joint attention over a sequence held in two tensors (README, "Attention
+ * sink for MMDiT": MMDiT blocks attend over the text and image token streams
+ * as one sequence, with the text block as the sink: sink_idx 0 when the text
+ * comes first, -1 when it comes last). Tokens [0, L0) of the sequence are in
+ * the q, k, v (and o) arguments, which then hold L0 tokens; tokens [L0, L)
+ * are in q1, k1, v1 (and o1), which hold L - L0 tokens. Both parts have the
+ * shape's layout and dtype; shape->L is the joint length. No concatenated
+ * copy is made: the kernels address each token in its own tensor. The
+ * segment boundary need not fall on a block boundary.
+ * Requires 1 <= L0 <= L; when L0 < L, the second-segment pointers the call
+ * reads or writes are non-NULL and 16-byte aligned (L0 == L: they are
+ * ignored). Otherwise PISA_EINVAL. A NULL pisa_segments_t is the
+ * one-tensor case. */
+typedef struct {
+  int32_t L0;
+  const void *q1, *k1, *v1;
+  void *o1;
+} pisa_segments_t;
+
+/* pisa_block_stats on a two-part sequence (reads seg->q1, k1, v1). */
+pisa_status_t pisa_block_stats_seg(const pisa_shape_t *shape, const void *q, const void *k,
+                                   const void *v, const pisa_segments_t *seg,
+                                   const pisa_stats_t *st, void *stream);
+
+/* pisa_attn_fwd on a two-part sequence (reads seg->q1, writes seg->o1). st
+ * comes from pisa_block_stats_seg with the same segments; pisa_select is
+ * unchanged. */
+pisa_status_t pisa_attn_fwd_seg(const pisa_shape_t *shape, const void *q, const pisa_stats_t *st,
+                                int32_t first_order, const int32_t *idx, int32_t topk,
+                                double scale, void *o, const pisa_segments_t *seg, void *stream);
+
+/* dense_attn_fwd on a two-part sequence (reads seg->q1, k1, v1, writes o1). */
+pisa_status_t dense_attn_fwd_seg(const pisa_shape_t *shape, const void *q, const void *k,
+                                 const void *v, const pisa_segments_t *seg, double scale, void *o,
+                                 void *ws, size_t ws_bytes, void *stream);
+
 /* Human-readable text of a status code (static storage). */
 const char *pisa_status_string(pisa_status_t status);
 

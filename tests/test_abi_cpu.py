@@ -119,3 +119,28 @@ def test_topk_rule_matches_table():
              (0.05, 591): 29, (1.0, 591): 591, (0.0, 5): 1}
     for (d, n), k in cases.items():
         assert bsa.topk_from_density(d, n) == k
+
+
+def test_segment_arguments_rejected():
+    """Two-part sequences: L0 outside [1, L], or a missing or misaligned
+    second-part tensor when L0 < L, fail before anything is enqueued."""
+    lib = bsa.load_library()
+    s = shape()  # L = 1000
+    st = stats_struct()
+    E = bsa.PISA_EINVAL
+
+    def seg(L0=600, q1=FAKE, k1=FAKE, v1=FAKE, o1=FAKE):
+        return ctypes.byref(bsa.Segments(L0, q1, k1, v1, o1))
+
+    stats = lambda g: lib.pisa_block_stats_seg(ctypes.byref(s), FAKE, FAKE, FAKE, g, ctypes.byref(st), None)
+    fwd = lambda g: lib.pisa_attn_fwd_seg(ctypes.byref(s), FAKE, ctypes.byref(st), 1, FAKE, 2, 0.1, FAKE,
+                                          g, None)
+    dense = lambda g: lib.dense_attn_fwd_seg(ctypes.byref(s), FAKE, FAKE, FAKE, g, 0.1, FAKE, FAKE,
+                                             1 << 40, None)
+    for call in (stats, fwd, dense):
+        assert call(seg(L0=0)) == E and call(seg(L0=-5)) == E and call(seg(L0=1001)) == E
+        assert call(seg(q1=None)) == E and call(seg(q1=FAKE + 8)) == E
+    assert stats(seg(k1=None)) == E and stats(seg(v1=FAKE + 4)) == E
+    assert fwd(seg(o1=None)) == E
+    assert dense(seg(k1=None)) == E and dense(seg(o1=None)) == E
+

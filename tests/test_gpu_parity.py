@@ -165,6 +165,80 @@ def test_random_small_shapes(w):
     check_workload(w)
 
 
+JOINT_CASES = [
+    # (workload, first-part length L0, layout): text first on a block boundary
+    # (FLUX's 512 text tokens), image first with the boundary inside a block
+    # (text last, Hunyuan-style), a 128-token block cut at 130, fp32, pb1
+    (W("joint_flux_like", 1, 2, 4608, 128, 64, 0.15, "bf16", "hyd", 0, 0.1, seed=71), 512, "BHLD"),
+    (W("joint_text_last", 1, 2, 1256, 128, 64, 0.2, "bf16", "pb1", -1, 0.0, seed=72), 1000, "BLHD"),
+    (W("joint_blk128_f32", 2, 1, 700, 64, 128, 0.3, "f32", "0th", None, 0.0, seed=73), 130, "BHLD"),
+    (W("joint_one_token_first", 1, 2, 900, 128, 64, 0.25, "bf16", "hyd", 0, 0.0, seed=74), 1, "BLHD"),
+]
+
+
+@pytest.mark.parametrize("case", JOINT_CASES, ids=lambda c: c[0].name)
+def test_joint_sequence_matches_single_tensor(case):
+    """A sequence passed in two tensors (tokens [0, L0) and [L0, L)) gives the
+    same statistics, selection and output bits as the same sequence in one
+    tensor, whose parity with the oracle the other tests check; the dense
+    baseline likewise."""
+    w, L0, layout = case
+    q, k, v = synth.make_qkv(w)
+    dev = torch.device("cuda:0")
+    ax = 2 if layout == "BHLD" else 1
+    full = [x.to(dev) if layout == "BHLD" else x.transpose(1, 2).contiguous().to(dev) for x in (q, k, v)]
+    parts = [(x.narrow(ax, 0, L0).contiguous(), x.narrow(ax, L0, w.L - L0).contiguous()) for x in full]
+    (q0, q1), (k0, k1), (v0, v1) = parts
+    n = w.n_blocks
+    topk = bsa.topk_from_density(w.density, n)
+    st = bsa.block_stats(*full, w.block, want_mnorm=w.cov_weight > 0, layout=layout)
+    idx = bsa.select(st, topk, w.scale, w.cov_weight, w.sink_idx)
+    o = bsa.attn_fwd(full[0], st, idx, w.scale, w.variant)
+    od = bsa.dense(*full, w.scale, layout=layout)
+    st2 = bsa.block_stats_seg(q0, k0, v0, q1, k1, v1, w.block, want_mnorm=w.cov_weight > 0, layout=layout)
+    idx2 = bsa.select(st2, topk, w.scale, w.cov_weight, w.sink_idx)
+    o0, o1 = bsa.attn_fwd_seg(q0, q1, st2, idx2, w.scale, w.variant)
+    d0, d1 = bsa.dense_seg(q0, k0, v0, q1, k1, v1, w.scale, layout=layout)
+    torch.cuda.synchronize()
+    for name in ("qbar", "kbar", "vsum", "hbar") + (("mnorm",) if w.cov_weight > 0 else ()):
+        assert torch.equal(getattr(st, name), getattr(st2, name)), name
+    assert torch.equal(idx, idx2)
+    assert torch.equal(torch.cat([o0, o1], ax), o)
+    assert torch.equal(torch.cat([d0, d1], ax), od)
+
+
+def test_mmdit_joint_attention_text_sink():
+    """The adapter puts the text block in every selection (block 0 with the
+    text first, block n-1 with it last) and returns the text and image outputs
+    of the joint sequence, compared here with the oracle on the concatenated
+    sequence."""
+    H, D, Lt, Li = 2, 128, 256, 1000
+    w = W("mmdit_adapter", 1, H, Lt + Li, D, 64, 0.1, "bf16", "hyd", None, 0.0, seed=75)
+    q, k, v = synth.make_qkv(w)
+    n = w.n_blocks
+    topk = bsa.topk_from_density(w.density, n)
+    dev = torch.device("cuda:0")
+    for text_first in (True, False):
+        if text_first:
+            txt = [x[:, :, :Lt].contiguous().to(dev) for x in (q, k, v)]
+            img = [x[:, :, Lt:].contiguous().to(dev) for x in (q, k, v)]
+        else:
+            img = [x[:, :, :Li].contiguous().to(dev) for x in (q, k, v)]
+            txt = [x[:, :, Li:].contiguous().to(dev) for x in (q, k, v)]
+        o_txt, o_img, idx = bsa.mmdit_joint_attention(*txt, *img, density=w.density, text_first=text_first,
+                                                      return_idx=True)
+        torch.cuda.synchronize()
+        sink = 0 if text_first else n - 1
+        assert bool((idx == sink).any(dim=-1).all())
+        o = torch.cat([o_txt, o_img] if text_first else [o_img, o_txt], 2).float().cpu().numpy()
+        gidx = idx.cpu().numpy()
+        for h in range(H):
+            qh, kh, vh = (synth.as_f64(x[0, h]) for x in (q, k, v))
+            ref, ridx = oracle.head_forward(qh, kh, vh, block=64, topk=topk, scale=w.scale,
+                                            sink_idx=0 if text_first else -1, idx=gidx[0, h])
+            compare_out(o[0, h], ref, "bf16", f"mmdit text_first={text_first} head {h}")
+
+
 def test_tiny_config_full():
     check_workload(synth.TINY)
 
