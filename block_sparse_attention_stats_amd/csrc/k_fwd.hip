@@ -66,11 +66,15 @@ __device__ __forceinline__ auto io_row(const FwdArgs& a, long bh, int row) {
     const size_t off = (size_t)b * a.stride_b + (size_t)h * a.stride_h + (size_t)row * a.stride_l;
     if constexpr (OUT) return a.o + off; else return a.q + off;
   }
-  // The second part's fields are read here, where they are used, rather than
-  // held in scalar registers through the whole kernel.
-  const volatile FwdArgs& v = a;
-  const size_t off = (size_t)b * v.stride1_b + (size_t)h * v.stride1_h + (size_t)(row - a.L0) * v.stride1_l;
-  if constexpr (OUT) return (uint8_t*)v.o1 + off; else return (const uint8_t*)v.q1 + off;
+  // The second part's fields are loaded here, where they are used, from the
+  // kernel's argument segment (every kernel calling this takes one FwdArgs
+  // and nothing else), rather than held in scalar registers through the
+  // whole kernel. (A volatile reference to the argument itself would copy the
+  // struct to scratch memory.)
+  using kargs_t = const volatile FwdArgs __attribute__((address_space(4)));
+  kargs_t* v = (kargs_t*)__builtin_amdgcn_kernarg_segment_ptr();
+  const size_t off = (size_t)b * v->stride1_b + (size_t)h * v->stride1_h + (size_t)(row - a.L0) * v->stride1_l;
+  if constexpr (OUT) return (uint8_t*)v->o1 + off; else return (const uint8_t*)v->q1 + off;
 }
 
 // Register-array types of one wavefront's state.
