@@ -232,6 +232,15 @@ def select(st: Stats, topk: int, scale: float, cov_weight: float = 0.0, sink_idx
 VARIANTS = {"0th": 0, "hyd": 1, "pb1": 2}
 
 
+def _variant_code(first_order) -> int:
+    """pisa_attn_fwd's first_order argument: True / "hyd" 1, False / "0th" 0, "pb1" 2."""
+    if isinstance(first_order, str):
+        if first_order not in VARIANTS:
+            raise ValueError(f"unknown variant {first_order!r}; expected one of {sorted(VARIANTS)}")
+        return VARIANTS[first_order]
+    return 1 if first_order else 0
+
+
 def attn_fwd(q, st: Stats, idx: torch.Tensor, scale: float, first_order=True,
              out: torch.Tensor | None = None) -> torch.Tensor:
     """Step 3: fused exact + zeroth-order (+ first-order) pass.
@@ -239,12 +248,7 @@ def attn_fwd(q, st: Stats, idx: torch.Tensor, scale: float, first_order=True,
     first_order: True or "hyd" (global H̄ term), False or "0th" (none), "pb1"
     (each unselected block's own first-order term)."""
     _check_qkv(q)
-    if isinstance(first_order, str):
-        if first_order not in VARIANTS:
-            raise ValueError(f"unknown variant {first_order!r}; expected one of {sorted(VARIANTS)}")
-        code = VARIANTS[first_order]
-    else:
-        code = 1 if first_order else 0
+    code = _variant_code(first_order)
     if idx.dtype != torch.int32 or not idx.is_contiguous() or not idx.is_cuda:
         raise ValueError("idx must be a contiguous int32 GPU tensor")
     shape = st.shape
@@ -354,7 +358,7 @@ def attn_fwd_seg(q0, q1, st: Stats, idx: torch.Tensor, scale: float, first_order
     _check_qkv(q1)
     if idx.dtype != torch.int32 or not idx.is_contiguous() or not idx.is_cuda:
         raise ValueError("idx must be a contiguous int32 GPU tensor")
-    code = VARIANTS[first_order] if isinstance(first_order, str) else (1 if first_order else 0)
+    code = _variant_code(first_order)
     shape = st.shape
     layout = "BLHD" if shape.layout == LAYOUTS["BLHD"] else "BHLD"
     L0 = shape.L - make_shape(q1, shape.block, layout).L
