@@ -59,7 +59,7 @@ def test_worked_example_stats(golden):
     np.testing.assert_array_equal(oracle.select_topk(S, 1), np.array(g["idx"]))
 
 
-@pytest.mark.parametrize("variant", ["hyd", "0th"])
+@pytest.mark.parametrize("variant", ["hyd", "0th", "pb1"])
 def test_worked_example_terms(golden, variant):
     """N_t and D_t term by term against the hand-derived closed forms."""
     g = golden
@@ -69,7 +69,8 @@ def test_worked_example_terms(golden, variant):
     for row in g["rows"]:
         t = row["t"]
         i = t // 2
-        Nt, Dt, m = oracle.pisa_rows(q, k, v, st, idx[i], i, 2, 1.0, variant == "hyd")
+        Nt, Dt, m = oracle.pisa_rows(q, k, v, st, idx[i], i, 2, 1.0, variant == "hyd",
+                                     per_block=variant == "pb1")
         r = t % 2
         N_exp = [closed_form(c) for c in row["N_" + variant]]
         D_exp = closed_form(row["D"])
@@ -80,7 +81,7 @@ def test_worked_example_terms(golden, variant):
 def test_worked_example_outputs(golden):
     g = golden
     q, k, v = (np.array(g["inputs"][x], dtype=np.float64) for x in "qkv")
-    for variant in ("hyd", "0th"):
+    for variant in ("hyd", "0th", "pb1"):
         o, idx = oracle.head_forward(q, k, v, block=2, topk=1, scale=1.0, variant=variant)
         exp = np.array([[closed_form(c) for c in row["N_" + variant]] for row in g["rows"]])
         exp /= np.array([closed_form(row["D"]) for row in g["rows"]])[:, None]
