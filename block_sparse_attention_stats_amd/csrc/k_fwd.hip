@@ -284,8 +284,9 @@ __device__ __forceinline__ void xstep(typename Regs<bf16, D>::Acc& oacc,
   // element g-1 is exponentiated, and the pair ending at element g-2 is rounded
   // and summed; two groups without an MFMA drain it. Without LAG each group
   // finishes its own element. Measured at the Wan shape, the lag speeds up the
-  // dense sweep (every tile an L2 hit) by 3% and slows the sparse one, whose
-  // gathers wait on memory, by 5%.
+  // dense sweep (every tile an L2 hit) by 3% and, with the present generation
+  // wait, the sparse pass by 1.4-1.9% (Wan and Hunyuan, densities 0.125 and
+  // 0.25), so every bf16 sweep uses it.
   constexpr int LG = LAG ? EPM : 0;
 #pragma unroll
   for (int mi = 0; mi < NM + (LAG ? 2 : 0); ++mi) {
@@ -701,7 +702,7 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
           for (int r = 0; r < 16; ++r) v[r] = ((dead >> vkey(r, h)) & 1u) ? kNegInf : 0.0f;
           return v;
         };
-        pipelined<T, D, DENSE>(
+        pipelined<T, D, true>(
             a.nct, a.kbp, a.vbp, [&](int ct) -> size_t { return (head_ct + ct) * G::SUB_BYTES; },
             cinit, cinit, asum, m, cs, qr, oacc, w, lane);
       } else {
@@ -758,7 +759,7 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
       for (int r = 0; r < 16; ++r) v[r] = vkey(r, h) >= nvalid ? kNegInf : 0.0f;
       return v;
     };
-    pipelined<T, D, DENSE>(
+    pipelined<T, D, true>(
         nt, a.kp, a.vp, off, [](int) { return f32x16{}; }, init, l, m, cs, qr, oacc, w, lane);
     after_exact();
     if (!centroids_first) phase2();
