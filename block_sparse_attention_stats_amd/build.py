@@ -34,6 +34,27 @@ def _compile(src: str) -> str:
     return out
 
 
+C_CALLER_SRC = os.path.join(ROOT, "tests", "c_abi", "pisa_c_caller.c")
+C_CALLER = os.path.join(ROOT, "tests", "c_abi", "pisa_c_caller")
+
+
+def build_c_caller(verbose: bool = False) -> str:
+    """The plain C caller of the ABI (a test fixture): gcc, C99, linked to the
+    in-tree libpisa.so and the HIP runtime."""
+    rocm = os.environ.get("ROCM_PATH", "/opt/rocm")
+    cmd = ["gcc", "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I" + os.path.join(rocm, "include"), "-I" + os.path.join(ROOT, "include"),
+           C_CALLER_SRC, "-o", C_CALLER, "-L" + PKG, "-lpisa", "-L" + os.path.join(rocm, "lib"),
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN/../../block_sparse_attention_stats_amd",
+           "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"gcc failed for the C caller:\n{r.stderr}")
+    if verbose:
+        print("built", C_CALLER)
+    return C_CALLER
+
+
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
@@ -46,6 +67,7 @@ def build(verbose: bool = False) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)
+    build_c_caller(verbose)
     return LIB
 
 

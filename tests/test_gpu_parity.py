@@ -6,6 +6,9 @@ configuration as the bench and are compared on sampled heads and query blocks
 that the oracle evaluates one by one.
 """
 
+import os
+import subprocess
+
 import numpy as np
 import pytest
 import torch
@@ -237,6 +240,41 @@ def test_mmdit_joint_attention_text_sink():
             ref, ridx = oracle.head_forward(qh, kh, vh, block=64, topk=topk, scale=w.scale,
                                             sink_idx=0 if text_first else -1, idx=gidx[0, h])
             compare_out(o[0, h], ref, "bf16", f"mmdit text_first={text_first} head {h}")
+
+
+C_CALLER = os.path.join(os.path.dirname(os.path.abspath(__file__)), "c_abi", "pisa_c_caller")
+
+
+@pytest.mark.parametrize("w", [SMALL[0], SMALL[5], PB1[1]], ids=lambda w: w.name)
+def test_plain_c_caller_matches_binding(w, tmp_path):
+    """tests/c_abi/pisa_c_caller.c drives the three steps through include/pisa.h
+    alone (hipMalloc'd buffers, default stream, no Python or torch in that
+    process): its selection and output are bit-identical to the binding's on
+    the same inputs."""
+    assert os.path.exists(C_CALLER), "build() did not produce tests/c_abi/pisa_c_caller"
+    q, k, v = synth.make_qkv(w)
+    raw = (lambda x: x.view(torch.int16)) if w.dtype == "bf16" else (lambda x: x)
+    for name, x in (("q", q), ("k", k), ("v", v)):
+        raw(x).contiguous().numpy().tofile(str(tmp_path / f"{name}.bin"))
+    n = w.n_blocks
+    topk = bsa.topk_from_density(w.density, n)
+    sink = "none" if w.sink_idx is None else str(w.sink_idx)
+    dtype = bsa.PISA_BF16 if w.dtype == "bf16" else bsa.PISA_F32
+    (tmp_path / "shape.txt").write_text(
+        f"{w.B} {w.H} {w.L} {w.D} {w.block} {dtype} {topk} {sink} {bsa.VARIANTS[w.variant]} {w.scale!r}\n")
+    log(f"[{w.name}] running the C caller")
+    r = subprocess.run([C_CALLER, str(tmp_path)], capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    st = bsa.block_stats(qd, kd, vd, w.block)
+    idx = bsa.select(st, topk, w.scale, 0.0, w.sink_idx)
+    o = bsa.attn_fwd(qd, st, idx, w.scale, w.variant)
+    torch.cuda.synchronize()
+    c_idx = np.fromfile(str(tmp_path / "idx.bin"), dtype=np.int32).reshape(idx.shape)
+    np.testing.assert_array_equal(c_idx, idx.cpu().numpy())
+    c_o = np.fromfile(str(tmp_path / "o.bin"), dtype=np.int16 if w.dtype == "bf16" else np.float32)
+    np.testing.assert_array_equal(c_o.reshape(o.shape), raw(o.cpu()).numpy())
 
 
 def test_tiny_config_full():
