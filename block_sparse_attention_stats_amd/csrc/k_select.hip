@@ -7,11 +7,15 @@
 //   register-tiled fp64 GEMM through LDS
 //   (n x n x D per head: small next to the fused pass). The sink column gets
 //   +infinity.
-// k_topk: one workgroup per score row, held in LDS as order-preserving 64-bit
-//   keys; an MSB-first radix select (up to 8 passes of 8 bits) narrows down the
-//   k-th largest key T, stopping early once the bucket that holds it is to be
-//   taken whole; then two block scans take every key above it and the
-//   lowest-index keys equal to it, and emit the indices ascending.
+// Top-k of a row: the k-th largest key T is narrowed down by an MSB-first
+//   radix select over order-preserving 64-bit keys, stopping early once the
+//   bucket that holds it is to be taken whole; then every key above T and the
+//   lowest-index keys equal to it are taken, and the indices emitted ascending.
+//   k_topk_wave (rows of up to 2048 blocks): one wavefront per row, its keys in
+//   registers; each pass's 8-bit digit starts at the highest bit in which the
+//   remaining candidates still differ, so no pass is spent on the sign and
+//   exponent bits they share. k_topk (longer rows): one workgroup per row, the
+//   keys in LDS, fixed 8-bit digits. Both return the same set.
 #include "pisa_dev.h"
 #include "pisa_internal.h"
 
@@ -182,6 +186,133 @@ __global__ __launch_bounds__(256) void k_topk(TopkArgs a) {
   }
 }
 
+// Wave-wide OR / AND of a 64-bit value.
+__device__ inline unsigned long long wave_or64(unsigned long long x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x |= __shfl_xor(x, o);
+  return x;
+}
+__device__ inline unsigned long long wave_and64(unsigned long long x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x &= __shfl_xor(x, o);
+  return x;
+}
+
+// Orders the LDS accesses of one wavefront against each other (the DS unit
+// runs a wave's operations in issue order; the fence keeps the compiler from
+// moving them).
+__device__ inline void wave_lds_order() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+// One wavefront per row; key j lives in lane j % 64, slot j / 64 (KPL slots).
+template <int KPL>
+__global__ __launch_bounds__(256) void k_topk_wave(TopkArgs a, long rows) {
+  __shared__ int4 hist_all[4][64];  // 256 digit counts per wavefront
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const long row = (long)blockIdx.x * 4 + wv;
+  if (row >= rows) return;
+  int4* hist4 = hist_all[wv];
+  int* hist = reinterpret_cast<int*>(hist4);
+  const int n = a.n, k = a.topk;
+  int32_t* out = a.idx + row * (long)k;
+  if (k >= n) {
+    for (int j = lane; j < n; j += 64) out[j] = j;
+    return;
+  }
+  const double* S = a.scores + row * (long)n;
+  // all loads in flight at once: slots past the end read the row's last score
+  double x[KPL];
+#pragma unroll
+  for (int s = 0; s < KPL; ++s) x[s] = S[min(s * 64 + lane, n - 1)];
+  unsigned long long key[KPL];
+#pragma unroll
+  for (int s = 0; s < KPL; ++s) key[s] = order_key(x[s]);
+  unsigned long long prefix = 0, pmask = 0;
+  int kk = k;
+  for (;;) {
+    // bits in which the candidates (keys matching prefix under pmask) differ
+    unsigned long long vor = 0, vand = ~0ull;
+#pragma unroll
+    for (int s = 0; s < KPL; ++s) {
+      if (s * 64 + lane < n && (key[s] & pmask) == prefix) {
+        vor |= key[s];
+        vand &= key[s];
+      }
+    }
+    vor = wave_or64(vor);
+    vand = wave_and64(vand);
+    const unsigned long long diff = vor ^ vand;
+    if (diff == 0) {  // every candidate equals T: ties go by index below
+      prefix = vand;
+      pmask = ~0ull;
+      break;
+    }
+    const int top = 63 - __clzll(diff);
+    const int shift = top >= 7 ? top - 7 : 0;
+    pmask = top == 63 ? 0ull : (~0ull << (top + 1));  // shared by every candidate
+    prefix = vand & pmask;
+    hist4[lane] = make_int4(0, 0, 0, 0);
+    wave_lds_order();
+#pragma unroll
+    for (int s = 0; s < KPL; ++s)
+      if (s * 64 + lane < n && (key[s] & pmask) == prefix)
+        atomicAdd(&hist[(int)((key[s] >> shift) & 255)], 1);
+    wave_lds_order();
+    // lane l holds digits 255-4l .. 252-4l, counted from the top
+    const int4 h = hist4[63 - lane];
+    const int c[4] = {h.w, h.z, h.y, h.x};
+    const int tot = c[0] + c[1] + c[2] + c[3];
+    int incl = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const int before = incl - tot;
+    const bool mine = before < kk && kk <= incl;
+    int dg = 0, gt = 0, cnt = 0;
+    if (mine) {
+      int g = before;
+      bool found = false;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (!found && g + c[u] >= kk) {
+          dg = 255 - 4 * lane - u;
+          gt = g;
+          cnt = c[u];
+          found = true;
+        }
+        g += c[u];
+      }
+    }
+    const int src = __ffsll((unsigned long long)__ballot(mine)) - 1;
+    dg = __shfl(dg, src);
+    gt = __shfl(gt, src);
+    cnt = __shfl(cnt, src);
+    prefix |= (unsigned long long)dg << shift;
+    pmask |= 255ull << shift;
+    kk -= gt;
+    wave_lds_order();  // the next pass clears the counts only after they are read
+    if (cnt == kk || shift == 0) break;
+  }
+  // every key above prefix, and the kk lowest-index keys equal to it
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int eq_seen = 0, pos = 0;
+#pragma unroll
+  for (int s = 0; s < KPL; ++s) {
+    const int j = s * 64 + lane;
+    const unsigned long long km = key[s] & pmask;
+    const bool valid = j < n;
+    const bool above = valid && km > prefix, eq = valid && km == prefix;
+    const unsigned long long beq = __ballot(eq);
+    const bool sel = above || (eq && eq_seen + __popcll(beq & lt) < kk);
+    const unsigned long long bsel = __ballot(sel);
+    const int at = pos + __popcll(bsel & lt);
+    if (sel && at < k) out[at] = j;  // exactly k are selected; the bound only guards the row
+    pos += __popcll(bsel);
+    eq_seen += __popcll(beq);
+  }
+}
+
 hipError_t launch_scores(int D, const ScoreArgs& a, long bh, hipStream_t s) {
   const bool big = a.n >= 512;
   const int tm = big ? 128 : 64;
@@ -198,8 +329,23 @@ hipError_t launch_scores(int D, const ScoreArgs& a, long bh, hipStream_t s) {
 }
 
 hipError_t launch_topk(const TopkArgs& a, long rows, hipStream_t s) {
-  const size_t lds = (size_t)a.n * sizeof(unsigned long long);
-  hipLaunchKernelGGL(k_topk, dim3((unsigned)rows), dim3(256), lds, s, a);
+  const int slots = (a.n + 63) / 64;
+  if (slots > 32) {
+    const size_t lds = (size_t)a.n * sizeof(unsigned long long);
+    hipLaunchKernelGGL(k_topk, dim3((unsigned)rows), dim3(256), lds, s, a);
+    return hipGetLastError();
+  }
+  const dim3 grid((unsigned)((rows + 3) / 4));
+  switch ((slots + 3) / 4) {
+    case 1: hipLaunchKernelGGL(k_topk_wave<4>, grid, dim3(256), 0, s, a, rows); break;
+    case 2: hipLaunchKernelGGL(k_topk_wave<8>, grid, dim3(256), 0, s, a, rows); break;
+    case 3: hipLaunchKernelGGL(k_topk_wave<12>, grid, dim3(256), 0, s, a, rows); break;
+    case 4: hipLaunchKernelGGL(k_topk_wave<16>, grid, dim3(256), 0, s, a, rows); break;
+    case 5: hipLaunchKernelGGL(k_topk_wave<20>, grid, dim3(256), 0, s, a, rows); break;
+    case 6: hipLaunchKernelGGL(k_topk_wave<24>, grid, dim3(256), 0, s, a, rows); break;
+    case 7: hipLaunchKernelGGL(k_topk_wave<28>, grid, dim3(256), 0, s, a, rows); break;
+    default: hipLaunchKernelGGL(k_topk_wave<32>, grid, dim3(256), 0, s, a, rows); break;
+  }
   return hipGetLastError();
 }
 

@@ -131,6 +131,28 @@ def make_qkv(w: Workload, heads: list[tuple[int, int]] | None = None):
     return q, k, v
 
 
+def integer_qkv(B: int, H: int, L: int, D: int, seed: int, key_period: int | None = None,
+                amp: int = 4):
+    """q, k, v as CPU bf16 tensors [B, H, L, D] of small integers in [-amp, amp],
+    drawn uniformly by ``numpy.random.default_rng([seed, b, h])`` (q, k, then v).
+    With ``key_period`` p, key block j (64 tokens) repeats key block j mod p, so
+    whole groups of key blocks are equal. Integers of this size are exact in
+    bf16, and so are block means over 64 tokens and their dot products in fp64,
+    whatever the order of summation."""
+    import torch
+    out = [np.empty((B, H, L, D), dtype=np.float32) for _ in range(3)]
+    for b in range(B):
+        for h in range(H):
+            rng = np.random.default_rng([seed, b, h])
+            q, k, v = (rng.integers(-amp, amp + 1, size=(L, D)).astype(np.float32) for _ in range(3))
+            if key_period:
+                n = -(-L // CLUSTER)
+                src = np.arange(n) % key_period
+                k = np.concatenate([k[s * CLUSTER:(s + 1) * CLUSTER] for s in src])[:L]
+            out[0][b, h], out[1][b, h], out[2][b, h] = q, k, v
+    return tuple(torch.from_numpy(x).to(torch.bfloat16) for x in out)
+
+
 def as_f64(t) -> np.ndarray:
     """The exact fp64 values of a rounded tensor (bf16 and fp32 widen exactly)."""
     return t.double().numpy()

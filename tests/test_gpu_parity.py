@@ -168,6 +168,42 @@ def test_random_small_shapes(w):
     check_workload(w)
 
 
+# row lengths (blocks) for routing: one to eight register slots per lane of
+# the wavefront top-k (full and one past full), its longest row (2048), the
+# workgroup top-k beyond it, and the longest row the library takes
+ROUTE_N = [1, 2, 63, 64, 256, 257, 700, 1182, 1861, 2048, 2049, 8192]
+
+
+@pytest.mark.parametrize("n", ROUTE_N)
+def test_routing_exact_scores_and_ties(n):
+    """Selection over rows of n blocks matches the oracle's exactly: the inputs
+    are small integers, so every routing score is exact in fp64 on both sides
+    and neither summation order nor rounding can move a block across the k-th
+    place. First every key block distinct (ties only by chance), then key
+    blocks repeating with period 7, where each row holds 7 distinct scores and
+    the k-th place always falls inside a run of equal scores that must go to
+    the lowest indices. Several k per n, with and without a sink."""
+    H = 2 if n <= 2048 else 1
+    L = n * 64
+    dev = torch.device("cuda:0")
+    rows = np.arange(n) if n <= 2048 else np.array(sample_qblocks(n, 96, seed=n))
+    ks = sorted({bsa.topk_from_density(d, n) for d in (0.01, 0.125, 0.5)} | {max(1, n - 1)})
+    for period in (None, 7):
+        q, k, v = synth.integer_qkv(1, H, L, 64, seed=900 + n, key_period=period)
+        st = bsa.block_stats(q.to(dev), k.to(dev), v.to(dev), 64)
+        ora = [oracle.block_stats(*(synth.as_f64(x[0, h]) for x in (q, k, v)), 64) for h in range(H)]
+        for topk in ks:
+            for sink in (None, -1):
+                idx = bsa.select(st, topk, 0.125, 0.0, sink).cpu().numpy()
+                for h in range(H):
+                    S = oracle.pooled_scores(ora[h]["qbar"][rows], ora[h]["kbar"], 0.125, sink_idx=sink)
+                    ref = oracle.select_topk(S, topk)
+                    bad = np.nonzero((idx[0, h][rows] != ref).any(axis=1))[0]
+                    assert bad.size == 0, (f"n={n} period={period} topk={topk} sink={sink} head {h}: "
+                                           f"{bad.size} rows differ, first query block {rows[bad[0]]}")
+    log(f"routing n={n}: exact over {len(rows)} query blocks x {H} heads, k in {ks}")
+
+
 JOINT_CASES = [
     # (workload, first-part length L0, layout): text first on a block boundary
     # (FLUX's 512 text tokens), image first with the boundary inside a block
