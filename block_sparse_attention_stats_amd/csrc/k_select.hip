@@ -92,6 +92,88 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
   }
 }
 
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+// k_scores_mfma: the same scores on the fp64 matrix cores, for n >= 512.
+// Each wavefront computes 16·TR x 16·TC (query block, key block) pairs as
+// TR x TC products of v_mfma_f64_16x16x4f64 (A: row m = lane % 16,
+// k = lane / 16; B: k = lane / 16, column = lane % 16; D: element r of a
+// lane is row lane / 16 + 4r, column lane % 16); four wavefronts in a 2 x 2
+// square make a workgroup. The k index is mapped so that each lane reads four
+// consecutive d of its q̄ / k̄ row with one 32-byte load: in step s of a
+// 16-wide chunk at d0, k = g stands for d = d0 + 4g + s. Operands come
+// straight from global memory (the L2 holds a head's q̄ and k̄); the next chunk
+// is loaded while the current one is multiplied.
+template <int D, int TR, int TC>
+__global__ __launch_bounds__(256) void k_scores_mfma(ScoreArgs a) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int r0 = blockIdx.y * 32 * TR + 16 * TR * (wv >> 1);
+  const int c0 = blockIdx.x * 32 * TC + 16 * TC * (wv & 1);
+  if (r0 >= a.n || c0 >= a.n) return;
+  const long bh = blockIdx.z;
+  const double* qb = a.qbar + (size_t)bh * a.n * D + 4 * g;
+  const double* kb = a.kbar + (size_t)bh * a.n * D + 4 * g;
+  const double* pa[TR];
+  const double* pb[TC];
+#pragma unroll
+  for (int t = 0; t < TR; ++t)  // rows and columns past n: computed, not stored
+    pa[t] = qb + (size_t)min(r0 + 16 * t + c, a.n - 1) * D;
+#pragma unroll
+  for (int u = 0; u < TC; ++u) pb[u] = kb + (size_t)min(c0 + 16 * u + c, a.n - 1) * D;
+  f64x4 acc[TR][TC];
+#pragma unroll
+  for (int t = 0; t < TR; ++t)
+#pragma unroll
+    for (int u = 0; u < TC; ++u) acc[t][u] = f64x4{0.0, 0.0, 0.0, 0.0};
+  f64x4 A[TR], B[TC];
+#pragma unroll
+  for (int t = 0; t < TR; ++t) A[t] = *reinterpret_cast<const f64x4*>(pa[t]);
+#pragma unroll
+  for (int u = 0; u < TC; ++u) B[u] = *reinterpret_cast<const f64x4*>(pb[u]);
+#pragma unroll
+  for (int d0 = 0; d0 < D; d0 += 16) {
+    f64x4 An[TR], Bn[TC];
+    if (d0 + 16 < D) {
+#pragma unroll
+      for (int t = 0; t < TR; ++t) An[t] = *reinterpret_cast<const f64x4*>(pa[t] + d0 + 16);
+#pragma unroll
+      for (int u = 0; u < TC; ++u) Bn[u] = *reinterpret_cast<const f64x4*>(pb[u] + d0 + 16);
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int t = 0; t < TR; ++t)
+#pragma unroll
+        for (int u = 0; u < TC; ++u)
+          acc[t][u] = __builtin_amdgcn_mfma_f64_16x16x4f64(A[t][s], B[u][s], acc[t][u], 0, 0, 0);
+    if (d0 + 16 < D) {
+#pragma unroll
+      for (int t = 0; t < TR; ++t) A[t] = An[t];
+#pragma unroll
+      for (int u = 0; u < TC; ++u) B[u] = Bn[u];
+    }
+  }
+  double* out = a.scores + (size_t)bh * a.n * a.n;
+#pragma unroll
+  for (int u = 0; u < TC; ++u) {
+    const int j = c0 + 16 * u + c;
+    if (j >= a.n) continue;
+    const double cov = a.cov_weight != 0.0 ? a.cov_weight * a.mnorm[bh * a.n + j] : 0.0;
+#pragma unroll
+    for (int t = 0; t < TR; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = r0 + 16 * t + g + 4 * r;
+        if (i >= a.n) continue;
+        double sc = a.scale * acc[t][u][r];
+        if (a.cov_weight != 0.0) sc = sc + cov;
+        if (j == a.sink_block) sc = __builtin_huge_val();
+        out[(size_t)i * a.n + j] = sc;
+      }
+  }
+}
+
 // Monotone map from fp64 to uint64: larger value -> larger key (-0 == +0).
 __device__ inline unsigned long long order_key(double x) {
   if (x == 0.0) x = 0.0;
@@ -313,18 +395,25 @@ __global__ __launch_bounds__(256) void k_topk_wave(TopkArgs a, long rows) {
   }
 }
 
+// MFMA products per wavefront of k_scores_mfma (rows x columns of 16 x 16).
+// 4 x 4 needs ~300 registers (one wavefront per SIMD) and still beats 4 x 2
+// and 2 x 2, which fit two and four: fewer operand loads per product count
+// for more than occupancy here.
+constexpr int kScoreTR = 4, kScoreTC = 4;
+
 hipError_t launch_scores(int D, const ScoreArgs& a, long bh, hipStream_t s) {
-  const bool big = a.n >= 512;
-  const int tm = big ? 128 : 64;
-  const unsigned t = (unsigned)((a.n + tm - 1) / tm);
-  dim3 grid(t, t, (unsigned)bh);
-  if (D == 64) {
-    if (big) hipLaunchKernelGGL((k_scores<64, 128>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_scores<64, 64>), grid, dim3(256), 0, s, a);
-  } else {
-    if (big) hipLaunchKernelGGL((k_scores<128, 128>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_scores<128, 64>), grid, dim3(256), 0, s, a);
+  if (a.n >= 512) {
+    constexpr int TR = kScoreTR, TC = kScoreTC;
+    dim3 grid((unsigned)((a.n + 32 * TC - 1) / (32 * TC)), (unsigned)((a.n + 32 * TR - 1) / (32 * TR)),
+              (unsigned)bh);
+    if (D == 64) hipLaunchKernelGGL((k_scores_mfma<64, TR, TC>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_scores_mfma<128, TR, TC>), grid, dim3(256), 0, s, a);
+    return hipGetLastError();
   }
+  const unsigned t = (unsigned)((a.n + 63) / 64);
+  dim3 grid(t, t, (unsigned)bh);
+  if (D == 64) hipLaunchKernelGGL((k_scores<64, 64>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_scores<128, 64>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
