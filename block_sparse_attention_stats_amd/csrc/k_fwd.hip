@@ -730,9 +730,9 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
     // tiles, which every query tile of the head shares, and fills the time a
     // workgroup would otherwise spend in before_exact (the generation wait that
     // lines up the exact sweeps over the gathered blocks). For long sweeps it
-    // comes last: measured at the Wan shape, the exact sweeps of a new
-    // generation then keep the L2 to themselves while the previous one scans
-    // centroids, which is worth more than the shorter wait.
+    // comes last, after the point where a workgroup with a short centroid scan
+    // already counts as done for the generation wait; running it first there
+    // measured slower at the Wan and Hunyuan shapes.
     const bool centroids_first = nsel * spb < kCentroidsFirstBelow;
     if (centroids_first) phase2();
     before_exact();
@@ -836,11 +836,12 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
 // Per-block first-order variant. An unselected block j contributes
 // α_tj (ΣV_j + s q_t H_j) to N_t, which expands over the block's own keys as
 // Σ_n α_tj (1 + s q_t·(k_n − k̄_j)) v_n: the first-order Taylor expansion of
-// e^{ℓ_tn} about the centroid logit. So the variant is one sweep over every
-// key block with linear weights P = α_tj (1 + ℓ_tn − c_tj) on the unselected
-// blocks and exponential ones on the selected blocks, on the same MFMA operand
-// copies of K and V; no D×D matrix per block is stored or read. The centroid
-// logits c_tj come from the k̄ tiles, 64 blocks at a time, through LDS.
+// e^{ℓ_tn} about the centroid logit. So the variant visits every key block:
+// the selected ones with exponential weights (the hybrid's exact sweep), the
+// unselected ones with linear weights P = α_tj (1 + ℓ_tn − c_tj), on the same
+// MFMA operand copies of K and V; no D×D matrix per block is stored or read.
+// The centroid logits c_tj come from the k̄ tiles, 64 blocks at a time,
+// through LDS.
 
 // Linear weights of one sub-tile of an unselected block: P = a1·Sᵀ + b1 per
 // query row (a1 = α s, b1 = α (1 − s C)), and their row sums. RAGGED: keys past
@@ -873,8 +874,8 @@ __device__ __forceinline__ void weights_linear(const f32x16 (&sacc)[2], const fl
 // forms P(t+1); K and V double-buffered two tiles ahead; loads past the end
 // clamped to the last tile). wts(Sᵀ, P, t) forms tile t's weights in the
 // prologue and the last tiles; in the main loop, which never reaches the last
-// two tiles, bf16 takes the written-out xstep with P = fma(Sᵀ, A, B),
-// exponentiated where coef(t, A, B) returns true, and row sums into acc.
+// two tiles, bf16 takes the written-out xstep with the linear weights
+// P = fma(Sᵀ, A, B) of coef(t, A, B), and row sums into acc.
 template <typename T, int D, typename Off, typename Init, typename Wts, typename Coef>
 __device__ __forceinline__ void pipelined_w(int nt, const uint8_t* kbase, const uint8_t* vbase,
                                             const Off& off, const Init& init, const Wts& wts,
@@ -907,16 +908,10 @@ __device__ __forceinline__ void pipelined_w(int nt, const uint8_t* kbase, const 
   for (; t + 5 < nt; t += 2) {
     if constexpr (sizeof(T) == 2) {
       float A1[2], B1[2], A2[2], B2[2];
-      const bool e1 = coef(t + 1, A1, B1);
-      const bool e2 = coef(t + 2, A2, B2);
-      auto w1 = [&](float x, int qt) {
-        const float y = fmaf(x, A1[qt], B1[qt]);
-        return e1 ? __builtin_amdgcn_exp2f(y) : y;
-      };
-      auto w2 = [&](float x, int qt) {
-        const float y = fmaf(x, A2[qt], B2[qt]);
-        return e2 ? __builtin_amdgcn_exp2f(y) : y;
-      };
+      coef(t + 1, A1, B1);
+      coef(t + 2, A2, B2);
+      auto w1 = [&](float x, int qt) { return fmaf(x, A1[qt], B1[qt]); };
+      auto w2 = [&](float x, int qt) { return fmaf(x, A2[qt], B2[qt]); };
       xstep<D, true>(oacc, vc0, pa, kc0, qr, sa, f32x16{}, sb, pb, acc, w1, vbase + off(t + 2),
                      kbase + off(t + 4), w, lane);  // PV(t), Sᵀ(t+2), P(t+1)
       xstep<D, true>(oacc, vc1, pb, kc1, qr, sb, f32x16{}, sa, pa, acc, w2, vbase + off(t + 3),
@@ -969,15 +964,18 @@ __device__ __forceinline__ void pipelined_w(int nt, const uint8_t* kbase, const 
   }
 }
 
-// The per-block first-order pass of one 64-row query tile. `cl` is a 64 x 64
-// LDS array for the centroid logits (raw q·k̄, [block][query row]). The fast
+// The per-block first-order pass of one 64-row query tile. The selected blocks
+// take the hybrid's exponential sweep; then, 64 blocks at a time, the centroid
+// logits go to `cl` (a 64 x 64 LDS array, raw q·k̄, [block][query row]), the
+// group's unselected blocks are listed in `ul` (64 LDS entries), and a sweep
+// with linear weights only runs over them. The fast
 // kernel shifts every exponent by the Cauchy–Schwarz bound of the logits, as
 // the hybrid's fast kernel does; the careful kernel (a tile whose denominator
 // underflowed) first finds the largest exponent the tile actually uses: the
 // exact logits of its selected blocks and the centroid logits of the others.
 template <typename T, int D, bool CAREFUL, int SPB, typename Before, typename After>
 __device__ __forceinline__ void pb1_tile(const FwdArgs& a, long item, FwdShared<T, D>& sh,
-                                         typename Regs<T, D>::Xo& xo, float (*cl)[kSub],
+                                         typename Regs<T, D>::Xo& xo, float (*cl)[kSub], int* ul,
                                          const Before& before_sweep, const After& after_sweep) {
   using G = Geo<T, D>;
   constexpr int NC = G::NC, DT = G::DT, ESZ = G::ESZ, KW = G::KW;
@@ -1096,6 +1094,25 @@ __device__ __forceinline__ void pb1_tile(const FwdArgs& a, long item, FwdShared<
   }
 
   before_sweep();
+  {
+    // selected blocks: the hybrid's exact sweep (the short last block, if
+    // selected, is the selection's last entry and closes the same pipeline)
+    const bool ragged_last = ragged && block_at(nsel - 1) == a.n - 1;
+    const int nt_full = (nsel - (ragged_last ? 1 : 0)) * spb;
+    const int nt = nt_full + (ragged_last ? nsub_last : 0);
+    auto off = [&](int t) -> size_t {
+      return (head_sub + (size_t)block_at(t / spb) * spb + (t % spb)) * G::SUB_BYTES;
+    };
+    auto init = [&](int t) {
+      const int nvalid = t < nt_full ? kSub : a.n_last - kSub * (t - nt_full) - 32 * w;
+      f32x16 v;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[r] = vkey(r, h) >= nvalid ? kNegInf : 0.0f;
+      return v;
+    };
+    pipelined<T, D, true>(nt, a.kp, a.vp, off, [](int) { return f32x16{}; }, init, l, m, cs, qr,
+                          oacc, w, lane);
+  }
   for (int ct = 0; ct < a.nct; ++ct) {
     const int j0 = kSub * ct, j1 = min(j0 + kSub, a.n);
     {
@@ -1108,43 +1125,21 @@ __device__ __forceinline__ void pb1_tile(const FwdArgs& a, long item, FwdShared<
 #pragma unroll
         for (int r = 0; r < 16; ++r) cl[32 * w + vkey(r, h)][32 * qt + l32] = sx[qt][r];
     }
+    // the group's unselected blocks, ascending (both wavefronts count them;
+    // wavefront 0 writes the list)
+    const bool un = j0 + lane < j1 && !selected(j0 + lane);
+    const uint64_t ub = __ballot(un);
+    if (w == 0 && un) ul[__popcll(ub & ((1ull << lane) - 1ull))] = j0 + lane;
+    const int nu = __popcll(ub);
     __syncthreads();
-    const int g0 = j0 * spb;
-    const int nt = (ragged && j1 == a.n) ? g_last + nsub_last - g0 : (j1 - j0) * spb;
-    auto off = [&](int t) -> size_t { return (head_sub + g0 + t) * G::SUB_BYTES; };
-    auto init = [&](int t) { return init_g(g0 + t); };
-    auto wts = [&](const f32x16 (&sx)[2], typename Regs<T, D>::P& px, int t) {
-      const int g = g0 + t;
-      const int j = g / spb;
-      if (selected(j)) {
-        weights_full<T, D>(sx, m, l, px, cs);
-        return;
-      }
-      float a1[2], b1[2];
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        const float c = cl[j - j0][32 * qt + l32];
-        const float al = __builtin_amdgcn_exp2f(fmaf(c, cs, -m[qt]));
-        a1[qt] = al * a.scale;
-        b1[qt] = fmaf(-a1[qt], c, al);
-      }
-      if (ragged && g >= g_last)
-        weights_linear<T, D, true>(sx, a1, b1, l, px);
-      else
-        weights_linear<T, D, false>(sx, a1, b1, l, px);
-    };
-    // the same weights as fma(Sᵀ, A, B), exponentiated on selected blocks
-    // (tiles of the main loop are never the ragged last ones)
+    // the short last block, if unselected, is the list's last entry
+    const bool ragged_u = ragged && j1 == a.n && nu > 0 && !selected(a.n - 1);
+    const int nt = nu * spb - (ragged_u ? spb - nsub_last : 0);
+    auto gsub = [&](int t) { return ul[t / spb] * spb + t % spb; };
+    auto off = [&](int t) -> size_t { return (head_sub + gsub(t)) * G::SUB_BYTES; };
+    auto init = [&](int t) { return init_g(gsub(t)); };
     auto coef = [&](int t, float (&A)[2], float (&B)[2]) {
-      const int j = (g0 + t) / spb;
-      if (selected(j)) {
-#pragma unroll
-        for (int qt = 0; qt < 2; ++qt) {
-          A[qt] = cs;
-          B[qt] = -m[qt];
-        }
-        return true;
-      }
+      const int j = ul[t / spb];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) {
         const float c = cl[j - j0][32 * qt + l32];
@@ -1152,10 +1147,18 @@ __device__ __forceinline__ void pb1_tile(const FwdArgs& a, long item, FwdShared<
         A[qt] = al * a.scale;
         B[qt] = fmaf(-A[qt], c, al);
       }
-      return false;
     };
+    auto wts = [&](const f32x16 (&sx)[2], typename Regs<T, D>::P& px, int t) {
+      float a1[2], b1[2];
+      coef(t, a1, b1);
+      if (ragged && gsub(t) >= g_last)
+        weights_linear<T, D, true>(sx, a1, b1, l, px);
+      else
+        weights_linear<T, D, false>(sx, a1, b1, l, px);
+    };
+    // (tiles of the main loop are never the ragged last ones)
     pipelined_w<T, D>(nt, a.kp, a.vp, off, init, wts, coef, l, qr, oacc, w, lane);
-    __syncthreads();  // every wavefront is done with this tile's logits
+    __syncthreads();  // every wavefront is done with this group's logits and list
   }
   after_sweep();
 
@@ -1240,6 +1243,7 @@ __global__ __launch_bounds__(128, 1) void k_pisa_pb1(FwdArgs a) {
   __shared__ FwdShared<T, D> sh;
   __shared__ typename Regs<T, D>::Xo xo;
   __shared__ float cl[kSub][kSub];
+  __shared__ int ul[kSub];
   const long item = blockIdx.x;
   const long g = item / a.nwg;
   auto wait = [&]() {
@@ -1257,7 +1261,7 @@ __global__ __launch_bounds__(128, 1) void k_pisa_pb1(FwdArgs a) {
   auto done = [&]() {
     if (threadIdx.x == 0) __hip_atomic_fetch_add(a.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
-  pb1_tile<T, D, false, SPB>(a, item, sh, xo, cl, wait, done);
+  pb1_tile<T, D, false, SPB>(a, item, sh, xo, cl, ul, wait, done);
 }
 
 // The query tiles whose denominator underflowed under the fast kernel's shift,
@@ -1267,11 +1271,12 @@ __global__ __launch_bounds__(128, 1) void k_pisa_pb1_careful(FwdArgs a) {
   __shared__ FwdShared<T, D> sh;
   __shared__ typename Regs<T, D>::Xo xo;
   __shared__ float cl[kSub][kSub];
+  __shared__ int ul[kSub];
   const int count = *(volatile int*)a.redo;
   for (int e = blockIdx.x; e < count; e += gridDim.x) {
     const long item = a.redo[1 + e];
     __syncthreads();
-    pb1_tile<T, D, true, SPB>(a, item, sh, xo, cl, [] {}, [] {});
+    pb1_tile<T, D, true, SPB>(a, item, sh, xo, cl, ul, [] {}, [] {});
   }
 }
 
