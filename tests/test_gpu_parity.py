@@ -322,6 +322,28 @@ def test_flux_config_full():
     check_workload(synth.FLUX)
 
 
+# the longest sequences the library takes: 8192 key blocks (the per-tile
+# selection mask's size), with a ragged last block, both block sizes, all
+# three variants
+MAX_BLOCKS = [
+    W("max_blocks_blk64_hyd_sink_last", 1, 1, 8192 * 64 - 13, 64, 64, 0.01, "bf16", "hyd", -1, 0.0,
+      seed=81),
+    W("max_blocks_blk128_0th", 1, 1, 8192 * 128 - 100, 64, 128, 0.02, "bf16", "0th", None, 0.0,
+      seed=82),
+    W("max_blocks_blk64_pb1_sink0", 1, 1, 8192 * 64 - 40, 64, 64, 0.01, "bf16", "pb1", 0, 0.0, seed=83),
+]
+
+
+@pytest.mark.parametrize("w", MAX_BLOCKS, ids=lambda w: w.name)
+def test_longest_sequences_sampled(w):
+    """Statistics and selection of every query block, and the output of 24
+    sampled query blocks (the first and last among them), at the block count
+    limit; selection rows are checked with the tie rule, outputs against the
+    oracle as everywhere else."""
+    assert w.n_blocks == 8192
+    check_workload(w, qblock_sample=24)
+
+
 def test_wan_config_sampled():
     w = synth.WAN
     check_workload(w, heads=[(0, 0), (0, 17), (0, 39)], qblock_sample=10)
