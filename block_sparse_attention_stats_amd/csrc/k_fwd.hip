@@ -171,6 +171,11 @@ __device__ __forceinline__ void tile_weights(const f32x16 (&sacc)[2], const floa
       p[r] = __builtin_amdgcn_exp2f(fmaf(sacc[qt][r], cs, -ms));
       if constexpr (KIND != kExactFull) p[r] = dead_key<KIND>(r, h, w, valid, selword) ? 0.0f : p[r];
     }
+#pragma unroll
+    for (int c = 0; c < G::CPK; ++c) {
+      pc[qt][c] = Op<T>::pack(&p[G::KW * c]);
+      Op<T>::unpack(pc[qt][c], &p[G::KW * c]);  // the sums take the rounded weights
+    }
     float ps = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) ps += p[r];
@@ -184,16 +189,19 @@ __device__ __forceinline__ void tile_weights(const f32x16 (&sacc)[2], const floa
     } else {
       l[qt] += ps;
     }
-#pragma unroll
-    for (int c = 0; c < G::CPK; ++c) pc[qt][c] = Op<T>::pack(&p[G::KW * c]);
   }
 }
 
-// Weights of a full exact sub-tile (no masks): P = 2^(Sᵀ·cs − m) and the row
-// sums of its fp32 values. (The numerator takes P rounded to the operand type,
-// which is unbiased; summing the rounded values instead would need the packed
-// dot-product instruction, which stalls the matrix pipe on gfx950.)
-template <typename T, int D>
+// Weights of a full sub-tile: P = 2^(Sᵀ·cs − m) and its row sums. The
+// numerator takes P rounded to the operand type. With RSUM the sums take the
+// rounded values too (unpacked with two bit operations per pair), so that a
+// row whose weight sits on one key returns that key's value exactly; the
+// exact sweeps use it. The centroid scan keeps fp32 sums, which the fast
+// kernel's correction for the short last block (an fp32 weight recomputed in
+// the epilogue, times n_last − blk) must match. The written-out main loop
+// (xstep) sums fp32 values, as unbiased, and saves those operations where it
+// counts; a sweep's first and last tiles always come here.
+template <typename T, int D, bool RSUM>
 __device__ __forceinline__ void weights_full(const f32x16 (&sacc)[2], const float (&m)[2],
                                              float (&l)[2], typename Regs<T, D>::P& pc, float cs) {
   using G = Geo<T, D>;
@@ -206,6 +214,7 @@ __device__ __forceinline__ void weights_full(const f32x16 (&sacc)[2], const floa
       for (int e = 0; e < G::KW; ++e)
         p[e] = __builtin_amdgcn_exp2f(fmaf(sacc[qt][G::KW * c + e], cs, -m[qt]));
       pc[qt][c] = Op<T>::pack(p);
+      if constexpr (RSUM) Op<T>::unpack(pc[qt][c], p);
 #pragma unroll
       for (int e = 0; e < G::KW; e += 2) l[qt] += p[e] + p[e + 1];
     }
@@ -386,8 +395,8 @@ __device__ __forceinline__ void step(typename Regs<T, D>::Acc& oacc, const typen
 // may be a constant. The weights' row sums go to acc. Per tile t the MFMA pipe
 // runs PV(t) then Sᵀ(t+2) while the VALU forms P(t+1) from Sᵀ(t+1). K and V are double-buffered in registers: the
 // loads of V(t+2) and K(t+4) are issued during tile t, two tiles before use,
-// which hides the latency of gathers that miss the L2.
-template <typename T, int D, bool LAG, typename Off, typename InitL, typename Init>
+// which hides the latency of gathers that miss the L2. RSUM: see weights_full.
+template <typename T, int D, bool LAG, bool RSUM, typename Off, typename InitL, typename Init>
 __device__ __forceinline__ void pipelined(int nt, const uint8_t* kbase, const uint8_t* vbase,
                                           const Off& off, const InitL& init_loop, const Init& init,
                                           float (&acc)[2],
@@ -396,7 +405,7 @@ __device__ __forceinline__ void pipelined(int nt, const uint8_t* kbase, const ui
                                           typename Regs<T, D>::Acc& oacc, int w, int lane) {
   if (nt <= 0) return;
   auto wts = [&](const f32x16 (&sx)[2], typename Regs<T, D>::P& px) {
-    weights_full<T, D>(sx, m, acc, px, cs);
+    weights_full<T, D, RSUM>(sx, m, acc, px, cs);
   };
   auto wexp = [&](float x, int qt) { return __builtin_amdgcn_exp2f(fmaf(x, cs, -m[qt])); };
   typename Regs<T, D>::K kc0, kc1;
@@ -702,7 +711,7 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
           for (int r = 0; r < 16; ++r) v[r] = ((dead >> vkey(r, h)) & 1u) ? kNegInf : 0.0f;
           return v;
         };
-        pipelined<T, D, true>(
+        pipelined<T, D, true, false>(
             a.nct, a.kbp, a.vbp, [&](int ct) -> size_t { return (head_ct + ct) * G::SUB_BYTES; },
             cinit, cinit, asum, m, cs, qr, oacc, w, lane);
       } else {
@@ -759,7 +768,7 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
       for (int r = 0; r < 16; ++r) v[r] = vkey(r, h) >= nvalid ? kNegInf : 0.0f;
       return v;
     };
-    pipelined<T, D, true>(
+    pipelined<T, D, true, true>(
         nt, a.kp, a.vp, off, [](int) { return f32x16{}; }, init, l, m, cs, qr, oacc, w, lane);
     after_exact();
     if (!centroids_first) phase2();
@@ -863,6 +872,7 @@ __device__ __forceinline__ void weights_linear(const f32x16 (&sacc)[2], const fl
         p[e] = (RAGGED && sv == kNegInf) ? 0.0f : x;
       }
       pc[qt][c] = Op<T>::pack(p);
+      Op<T>::unpack(pc[qt][c], p);  // the sums take the rounded weights
 #pragma unroll
       for (int e = 0; e < G::KW; e += 2) l[qt] += p[e] + p[e + 1];
     }
@@ -1110,7 +1120,7 @@ __device__ __forceinline__ void pb1_tile(const FwdArgs& a, long item, FwdShared<
       for (int r = 0; r < 16; ++r) v[r] = vkey(r, h) >= nvalid ? kNegInf : 0.0f;
       return v;
     };
-    pipelined<T, D, true>(nt, a.kp, a.vp, off, [](int) { return f32x16{}; }, init, l, m, cs, qr,
+    pipelined<T, D, true, true>(nt, a.kp, a.vp, off, [](int) { return f32x16{}; }, init, l, m, cs, qr,
                           oacc, w, lane);
   }
   for (int ct = 0; ct < a.nct; ++ct) {

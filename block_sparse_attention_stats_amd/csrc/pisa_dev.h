@@ -56,6 +56,16 @@ struct Op<bf16> {
     for (int e = 0; e < 8; ++e) v[e] = (bf16)x[e];
     return __builtin_bit_cast(uint4, v);
   }
+  // The KW values of a packed chunk, widened exactly to fp32 (element 2i in
+  // the low half of word i).
+  __device__ static inline void unpack(const uint4& c, float* x) {
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(w[i] << 16);
+      x[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
   __device__ static inline float to_f32(bf16 x) { return (float)x; }
   __device__ static inline bf16 from_f32(float x) { return (bf16)x; }
   // acc + the sum of the KW rounded values held in one packed chunk
@@ -91,6 +101,11 @@ struct Op<float> {
   __device__ static inline uint4 pack(const float* x) {
     f32x4 v = {x[0], x[1], x[2], x[3]};
     return __builtin_bit_cast(uint4, v);
+  }
+  __device__ static inline void unpack(const uint4& c, float* x) {
+    const f32x4 v = __builtin_bit_cast(f32x4, c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = v[e];
   }
   __device__ static inline float to_f32(float x) { return x; }
   __device__ static inline float from_f32(float x) { return x; }

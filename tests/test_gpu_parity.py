@@ -45,6 +45,12 @@ EDGES = [
     W("edge_density_one", 1, 2, 600, 128, 64, 1.0, "bf16", "hyd", None, 0.0, seed=26),
     W("edge_density_one_f32", 1, 2, 333, 64, 128, 1.0, "f32", "0th", None, 0.0, seed=27),
     W("edge_topk_n_minus_1", 1, 2, 500, 128, 64, 0.99, "bf16", "hyd", 0, 0.0, seed=28),
+    # one token in bf16 (a single key: the output is v), and a one-token last
+    # block left to the zeroth-order term (its weight is the block-size sum
+    # corrected by n_last - blk)
+    W("edge_one_token_bf16_blk128_0th_sink0", 2, 1, 1, 64, 128, 0.1, "bf16", "0th", 0, 0.0, seed=5571),
+    W("edge_one_token_bf16_pb1_sink_last", 1, 1, 1, 128, 64, 0.3, "bf16", "pb1", -1, 0.0, seed=5608),
+    W("edge_last_block_one_token_0th_sink0", 1, 3, 65, 128, 64, 0.9, "bf16", "0th", 0, 0.0, seed=5296),
 ]
 
 
@@ -320,6 +326,24 @@ def test_tiny_config_full():
 
 def test_flux_config_full():
     check_workload(synth.FLUX)
+
+
+@pytest.mark.parametrize("variant", ["hyd", "0th", "pb1"])
+def test_single_token_returns_v_exactly(variant):
+    """A one-token sequence has a single key, whose softmax weight is 1, so
+    o = v. In bf16 the kernels return v bit for bit: the numerator and the
+    denominator take the same rounded weight, and the quotient is within an
+    fp32 rounding of v, which rounds back to v."""
+    dev = torch.device("cuda:0")
+    for seed, (D, blk) in enumerate([(64, 64), (128, 64), (64, 128), (128, 128)] * 2):
+        w = W(f"one_token_{variant}_{seed}", 2, 3, 1, D, blk, 1.0, "bf16", variant, [None, 0, -1][seed % 3],
+              0.0, seed=700 + seed)
+        q, k, v = (x.to(dev) for x in synth.make_qkv(w))
+        st = bsa.block_stats(q, k, v, blk)
+        idx = bsa.select(st, 1, w.scale, 0.0, w.sink_idx)
+        o = bsa.attn_fwd(q, st, idx, w.scale, variant)
+        torch.cuda.synchronize()
+        assert torch.equal(o, v), f"{w.name}: max diff {(o.float() - v.float()).abs().max().item()}"
 
 
 # the longest sequences the library takes: 8192 key blocks (the per-tile
