@@ -152,7 +152,8 @@ def test_blhd_layout_matches_bhld(w):
             compare_out(o2[0, :, h].float().cpu().numpy(), o_ref, w.dtype, f"BLHD head {h}")
 
 
-def random_cases(count: int, seed: int):
+def random_cases(count: int, seed: int, lengths=(1, 63, 64, 65, 127, 129, 500, 1000, 1777, 2600),
+                 prefix: str = "rand"):
     """Seeded random small workloads over every option: length (ragged tails of
     any size, a single token), head dim, block size, density (topk 1 to n),
     variant, I/O dtype, sink and covariance weight."""
@@ -160,8 +161,8 @@ def random_cases(count: int, seed: int):
     out = []
     for c in range(count):
         blk = int(rng.choice([64, 128]))
-        L = int(rng.choice([1, 63, 64, 65, 127, 129, 500, 1000, 1777, 2600]))
-        out.append(W(f"rand{c}", int(rng.integers(1, 3)), int(rng.integers(1, 4)), L,
+        L = int(rng.choice(lengths))
+        out.append(W(f"{prefix}{c}", int(rng.integers(1, 3)), int(rng.integers(1, 4)), L,
                      int(rng.choice([64, 128])), blk, float(rng.choice([0.02, 0.1, 0.3, 0.6, 1.0])),
                      str(rng.choice(["bf16", "f32"])), str(rng.choice(["hyd", "0th", "pb1"])),
                      [None, 0, -1][int(rng.integers(0, 3))], float(rng.choice([0.0, 0.0, 1e-3, 0.1])),
@@ -171,6 +172,14 @@ def random_cases(count: int, seed: int):
 
 @pytest.mark.parametrize("w", random_cases(24, 2026), ids=lambda w: w.name)
 def test_random_small_shapes(w):
+    check_workload(w)
+
+
+# longer sequences too (up to 15000 tokens, several hundred blocks)
+@pytest.mark.parametrize("w", random_cases(40, 4243, lengths=(1, 17, 64, 65, 200, 777, 1500, 3000, 4100,
+                                                              6000, 9001, 15000), prefix="wide"),
+                         ids=lambda w: w.name)
+def test_random_wider_shapes(w):
     check_workload(w)
 
 
