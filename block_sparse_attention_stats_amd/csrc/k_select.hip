@@ -2,11 +2,10 @@
 // 2602.01077, section 2 "Covariance-Aware Routing"; the authors' README,
 // "Attention sink for MMDiT").
 //
-// k_scores: S_ij = scale * q̄_i·k̄_j + cov_weight * M_j in fp64 for 128x128 (or,
-//   for small n, 64x64) tiles of (query block, key block) pairs, a
-//   register-tiled fp64 GEMM through LDS
-//   (n x n x D per head: small next to the fused pass). The sink column gets
-//   +infinity.
+// Scores: S_ij = scale * q̄_i·k̄_j + cov_weight * M_j in fp64 over (query block,
+//   key block) tiles (n x n x D per head: small next to the fused pass); the
+//   sink column gets +infinity. k_scores_mfma (n >= 512) on the fp64 matrix
+//   cores; k_scores (shorter rows) a register-tiled fp64 GEMM through LDS.
 // Top-k of a row: the k-th largest key T is narrowed down by an MSB-first
 //   radix select over order-preserving 64-bit keys, stopping early once the
 //   bucket that holds it is to be taken whole; then every key above T and the
@@ -22,8 +21,8 @@
 namespace pisa {
 
 // k_scores tile: TM x TM (query block, key block) pairs per workgroup, each of
-// the 256 threads owning an (TM/16) x (TM/16) block of them. 128 for long
-// sequences (8 FMAs per LDS value read), 64 when n is small.
+// the 256 threads owning an (TM/16) x (TM/16) block of them (TM = 64 for the
+// rows it serves, n < 512).
 template <int D, int TM>
 __global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
   // Rows ty + 16x, columns tx + 16y. The dot products run over d in order, one
