@@ -122,14 +122,62 @@ def _dtype_code(t: torch.Tensor) -> int:
 def _check_qkv(*ts: torch.Tensor):
     ref = ts[0]
     for t in ts:
-        if not t.is_cuda:
-            raise ValueError("tensors must be on the GPU")
+        if not isinstance(t, torch.Tensor):
+            raise TypeError("q, k, v must be torch tensors")
         if t.dim() != 4:
-            raise ValueError("tensors must be [batch, heads, seq, head_dim]")
+            raise ValueError("tensors must be [batch, heads, seq, head_dim] or [batch, seq, heads, head_dim]")
         if t.shape != ref.shape or t.dtype != ref.dtype or t.device != ref.device:
             raise ValueError("q, k, v must share shape, dtype and device")
         if not t.is_contiguous():
             raise ValueError("tensors must be contiguous")
+
+
+def _on_gpu(*ts: torch.Tensor):
+    """Every tensor on one GPU (checked after shapes and dtypes, so that a
+    mismatch is reported as such on any device)."""
+    dev = ts[0].device
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if t.device != dev:
+            raise ValueError("tensors must be on the same GPU")
+
+
+def _expect(t, shape, dtype, what: str):
+    """t is a contiguous tensor of exactly `shape` and `dtype` (device checked later)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{what} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+_TORCH_DTYPE = {0: torch.float32, 1: torch.bfloat16}
+
+
+def _io_shape(shape: "Shape", L: int | None = None) -> tuple:
+    """Shape of a q, k, v or o tensor holding L tokens (default: all) of `shape`."""
+    L = shape.L if L is None else L
+    return (shape.B, L, shape.H, shape.D) if shape.layout == 1 else (shape.B, shape.H, L, shape.D)
+
+
+def _check_io(t, shape: "Shape", what: str, L: int | None = None):
+    _expect(t, _io_shape(shape, L), _TORCH_DTYPE[shape.dtype], what)
+
+
+def _check_idx(idx, shape: "Shape") -> int:
+    """idx is [B, H, n, topk] int32 with 1 <= topk <= n; returns topk."""
+    if not isinstance(idx, torch.Tensor) or idx.dim() != 4:
+        raise ValueError("idx must be a [batch, heads, blocks, topk] tensor")
+    n = num_blocks(shape.L, shape.block)
+    topk = int(idx.shape[-1])
+    if not 1 <= topk <= n:
+        raise ValueError(f"idx holds {topk} blocks per row; expected 1 to {n}")
+    _expect(idx, (shape.B, shape.H, n, topk), torch.int32, "idx")
+    return topk
 
 
 def make_shape(q: torch.Tensor, block_size: int, layout: str = "BHLD") -> Shape:
@@ -169,10 +217,38 @@ class Stats:
     mnorm: torch.Tensor | None  # [B,H,n] fp64
     ws: torch.Tensor     # uint8 workspace
 
+    def check(self, shape: Shape | None = None):
+        """Every buffer has the size and dtype that the shape (default: its
+        own) implies; raises ValueError otherwise. The device is checked by
+        the caller, with the call's other tensors (tensors())."""
+        sh = self.shape
+        if shape is not None and _shape_tuple(shape) != _shape_tuple(sh):
+            raise ValueError(f"statistics were made for shape {_shape_tuple(sh)}, "
+                             f"not {_shape_tuple(shape)}")
+        n = num_blocks(sh.L, sh.block)
+        f64 = torch.float64
+        _expect(self.qbar, (sh.B, sh.H, n, sh.D), f64, "Stats.qbar")
+        _expect(self.kbar, (sh.B, sh.H, n, sh.D), f64, "Stats.kbar")
+        _expect(self.vsum, (sh.B, sh.H, n, sh.D), f64, "Stats.vsum")
+        _expect(self.hbar, (sh.B, sh.H, sh.D, sh.D), f64, "Stats.hbar")
+        if self.mnorm is not None:
+            _expect(self.mnorm, (sh.B, sh.H, n), f64, "Stats.mnorm")
+        if not isinstance(self.ws, torch.Tensor) or self.ws.dtype != torch.uint8 or self.ws.dim() != 1:
+            raise ValueError("Stats.ws must be a 1-D uint8 tensor")
+        if self.ws.numel() < workspace_bytes(sh):
+            raise ValueError(f"Stats.ws holds {self.ws.numel()} bytes; the shape needs {workspace_bytes(sh)}")
+
+    def tensors(self) -> list:
+        return [t for t in (self.qbar, self.kbar, self.vsum, self.hbar, self.mnorm, self.ws) if t is not None]
+
     def struct(self) -> StatsStruct:
         return StatsStruct(self.qbar.data_ptr(), self.kbar.data_ptr(), self.vsum.data_ptr(),
                            self.hbar.data_ptr(), self.mnorm.data_ptr() if self.mnorm is not None else None,
                            self.ws.data_ptr(), self.ws.numel())
+
+
+def _shape_tuple(shape: Shape) -> tuple:
+    return (shape.B, shape.H, shape.L, shape.D, shape.block, shape.dtype, shape.layout)
 
 
 def workspace_bytes(shape: Shape) -> int:
@@ -199,6 +275,11 @@ def block_stats(q, k, v, block_size: int = 64, want_mnorm: bool = False, out: St
     statistics); the statistics themselves are [B,H,...] either way."""
     _check_qkv(q, k, v)
     shape = make_shape(q, block_size, layout)
+    if out is not None:
+        out.check(shape)
+        if want_mnorm and out.mnorm is None:
+            raise ValueError("want_mnorm needs Stats.mnorm")
+    _on_gpu(q, k, v, *(() if out is None else out.tensors()))
     st = out if out is not None else alloc_stats(shape, q.device, want_mnorm)
     sst = st.struct()
     _check(load_library().pisa_block_stats(ctypes.byref(shape), q.data_ptr(), k.data_ptr(),
@@ -219,7 +300,15 @@ def select(st: Stats, topk: int, scale: float, cov_weight: float = 0.0, sink_idx
            out: torch.Tensor | None = None) -> torch.Tensor:
     """Step 2: per-query-block top-k key blocks, ascending, [B,H,n,topk] int32."""
     shape = st.shape
+    st.check()
     n = num_blocks(shape.L, shape.block)
+    if not 1 <= int(topk) <= n:
+        raise ValueError(f"topk = {topk}; expected 1 to {n}")
+    if cov_weight and st.mnorm is None:
+        raise ValueError("covariance-aware routing (cov_weight > 0) needs Stats.mnorm")
+    if out is not None:
+        _expect(out, (shape.B, shape.H, n, int(topk)), torch.int32, "idx")
+    _on_gpu(*st.tensors(), *(() if out is None else (out,)))
     idx = out if out is not None else torch.empty((shape.B, shape.H, n, topk), dtype=torch.int32,
                                                   device=st.qbar.device)
     sst = st.struct()
@@ -247,15 +336,18 @@ def attn_fwd(q, st: Stats, idx: torch.Tensor, scale: float, first_order=True,
 
     first_order: True or "hyd" (global H̄ term), False or "0th" (none), "pb1"
     (each unselected block's own first-order term)."""
-    _check_qkv(q)
     code = _variant_code(first_order)
-    if idx.dtype != torch.int32 or not idx.is_contiguous() or not idx.is_cuda:
-        raise ValueError("idx must be a contiguous int32 GPU tensor")
     shape = st.shape
+    st.check()
+    _check_io(q, shape, "q")
+    topk = _check_idx(idx, shape)
+    if out is not None:
+        _check_io(out, shape, "out")
+    _on_gpu(q, idx, *st.tensors(), *(() if out is None else (out,)))
     o = out if out is not None else torch.empty_like(q)
     sst = st.struct()
     _check(load_library().pisa_attn_fwd(ctypes.byref(shape), q.data_ptr(), ctypes.byref(sst),
-                                        code, idx.data_ptr(), int(idx.shape[-1]),
+                                        code, idx.data_ptr(), topk,
                                         float(scale), o.data_ptr(), _stream()), "pisa_attn_fwd")
     return o
 
@@ -270,6 +362,12 @@ def dense(q, k, v, scale: float | None = None, out: torch.Tensor | None = None,
     nbytes = lib.dense_workspace_bytes(ctypes.byref(shape))
     if nbytes == 0:
         raise PisaError(PISA_EINVAL, "dense_workspace_bytes")
+    if out is not None:
+        _check_io(out, shape, "out")
+    if ws is not None:
+        if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+            raise ValueError("ws must be a contiguous 1-D uint8 tensor")
+    _on_gpu(q, k, v, *[t for t in (out, ws) if t is not None])
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     o = out if out is not None else torch.empty_like(q)
@@ -341,6 +439,11 @@ def block_stats_seg(q0, k0, v0, q1, k1, v1, block_size: int = 64, want_mnorm: bo
     _check_qkv(q1, k1, v1)
     shape = _joint_shape(q0, q1, block_size, layout)
     L0 = shape.L - make_shape(q1, block_size, layout).L
+    if out is not None:
+        out.check(shape)
+        if want_mnorm and out.mnorm is None:
+            raise ValueError("want_mnorm needs Stats.mnorm")
+    _on_gpu(q0, k0, v0, q1, k1, v1, *(() if out is None else out.tensors()))
     st = out if out is not None else alloc_stats(shape, q0.device, want_mnorm)
     sst = st.struct()
     seg = _segments(L0, q1, k1, v1)
@@ -354,20 +457,29 @@ def attn_fwd_seg(q0, q1, st: Stats, idx: torch.Tensor, scale: float, first_order
                  out0: torch.Tensor | None = None, out1: torch.Tensor | None = None):
     """Step 3 on the sequence q0 ++ q1; returns the output in two parts shaped
     like q0 and q1."""
-    _check_qkv(q0)
-    _check_qkv(q1)
-    if idx.dtype != torch.int32 or not idx.is_contiguous() or not idx.is_cuda:
-        raise ValueError("idx must be a contiguous int32 GPU tensor")
     code = _variant_code(first_order)
     shape = st.shape
-    layout = "BLHD" if shape.layout == LAYOUTS["BLHD"] else "BHLD"
-    L0 = shape.L - make_shape(q1, shape.block, layout).L
+    st.check()
+    if not isinstance(q1, torch.Tensor) or q1.dim() != 4:
+        raise ValueError("q1 must be a 4-D tensor")
+    L1 = int(q1.shape[1] if shape.layout == LAYOUTS["BLHD"] else q1.shape[2])
+    L0 = shape.L - L1
+    if not 1 <= L0 <= shape.L:
+        raise ValueError(f"q1 holds {L1} tokens; the statistics' sequence has {shape.L}")
+    _check_io(q0, shape, "q0", L0)
+    _check_io(q1, shape, "q1", L1)
+    topk = _check_idx(idx, shape)
+    if out0 is not None:
+        _check_io(out0, shape, "out0", L0)
+    if out1 is not None:
+        _check_io(out1, shape, "out1", L1)
+    _on_gpu(q0, q1, idx, *st.tensors(), *[t for t in (out0, out1) if t is not None])
     o0 = out0 if out0 is not None else torch.empty_like(q0)
     o1 = out1 if out1 is not None else torch.empty_like(q1)
     sst = st.struct()
     seg = _segments(L0, q1, o1=o1)
     _check(load_library().pisa_attn_fwd_seg(ctypes.byref(shape), q0.data_ptr(), ctypes.byref(sst), code,
-                                            idx.data_ptr(), int(idx.shape[-1]), float(scale),
+                                            idx.data_ptr(), topk, float(scale),
                                             o0.data_ptr(), ctypes.byref(seg), _stream()),
            "pisa_attn_fwd_seg")
     return o0, o1
@@ -379,6 +491,7 @@ def dense_seg(q0, k0, v0, q1, k1, v1, scale: float | None = None, layout: str = 
     _check_qkv(q1, k1, v1)
     shape = _joint_shape(q0, q1, 64, layout)
     L0 = shape.L - make_shape(q1, 64, layout).L
+    _on_gpu(q0, k0, v0, q1, k1, v1)
     s = 1.0 / math.sqrt(q0.shape[-1]) if scale is None else scale
     lib = load_library()
     nbytes = lib.dense_workspace_bytes(ctypes.byref(shape))

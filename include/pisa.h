@@ -18,8 +18,9 @@
  *   D_t = Σ_{j∈S_i} Σ_n e^{s q_t·k_n} + Σ_{j∈U_i} n_j α_tj.
  *
  * Conventions for every entry point:
- *  - Tensors q, k, v, o are DEVICE pointers to contiguous [B, H, L, D] arrays
- *    of the I/O dtype, owned by the caller, 16-byte aligned.
+ *  - Tensors q, k, v, o are DEVICE pointers to contiguous arrays of the I/O
+ *    dtype, [B, H, L, D] or [B, L, H, D] as shape->layout says, owned by the
+ *    caller, 16-byte aligned.
  *  - n = ceil(L / block) blocks per (batch, head); the last one holds
  *    n_last = L - (n-1)*block tokens.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
@@ -31,8 +32,9 @@
  *    returns PISA_EINVAL and enqueues nothing; a combination the library does
  *    not build returns PISA_ENOTSUP; a launch failure reported by the HIP
  *    runtime returns PISA_EHIP. No call aborts the process or throws.
- *  - The library keeps no global state and may be called from several host
- *    threads at once on different workspaces.
+ *  - The only state the library keeps is a per-host-thread copy of the text
+ *    of the last HIP error (pisa_last_hip_error). Calls from several host
+ *    threads at once are safe as long as they use different workspaces.
  */
 #ifndef PISA_H_
 #define PISA_H_
@@ -63,9 +65,10 @@ typedef enum { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype_t;
 #define PISA_LAYOUT_BLHD 1
 
 /* Problem shape. Supported: D in {64, 128}, block in {64, 128}, L >= 1,
- * B*H >= 1, dtype PISA_F32 or PISA_BF16 (I/O dtype; accumulation is fp32,
- * block statistics and routing scores are fp64), layout PISA_LAYOUT_BHLD or
- * PISA_LAYOUT_BLHD (a zero-initialised shape is BHLD). */
+ * B*H >= 1, n = ceil(L / block) <= 8192, dtype PISA_F32 or PISA_BF16 (the I/O
+ * dtype; see pisa_stats_t for the precision of each statistic; the fused
+ * pass accumulates in fp32), layout PISA_LAYOUT_BHLD or PISA_LAYOUT_BLHD (a
+ * zero-initialised shape is BHLD). */
 typedef struct {
   int32_t B, H, L, D, block;
   int32_t dtype;  /* pisa_dtype_t */
@@ -84,10 +87,22 @@ typedef struct {
  *   mnorm [B,H,n]   fp64  M_j = ||H_j - H̄||_F; may be NULL unless the
  *                         covariance-aware routing of pisa_select is used
  *   ws / ws_bytes         workspace of at least pisa_workspace_bytes(shape)
- *                         bytes, 256-byte aligned. pisa_block_stats writes
- *                         operand-ordered copies of K, V, k̄, ΣV and H̄ in the
- *                         I/O dtype there, which pisa_attn_fwd reads; its
- *                         content is otherwise unspecified. */
+ *                         bytes, 256-byte aligned (see below).
+ * Precision: q̄, k̄ and ΣV are fp64 sums of the inputs (exact for bf16),
+ * divided in fp64. H̄ is the mean of per-block H_j formed in fp32 on the
+ * matrix cores: the products k[d]·v[e] are exact for bf16 inputs, each run of
+ * consecutive blocks (up to 1024 tokens) is summed in one fp32 accumulator,
+ * from which k̄_j[d]·ΣV_j[e] (rounded to fp32) is subtracted as block j ends,
+ * and the runs are summed in fp64. M_j takes the block's fp32 sum of
+ * products, subtracts k̄_j[d]·ΣV_j[e] and H̄ in fp64, and sums the squares in
+ * fp64.
+ * The workspace: pisa_block_stats writes there the copies of K, V, k̄, ΣV and
+ * H̄ in the I/O dtype, laid out in the operand order of the fused kernel, and
+ * the largest key norms; pisa_select stages its routing scores there;
+ * pisa_attn_fwd reads the copies and resets and uses two counters there (the
+ * tiles left to its running-maximum kernel, and the arrival count that keeps
+ * its workgroups in step). A workspace therefore serves one call at a time:
+ * calls that share one must be ordered, e.g. on one stream. */
 typedef struct {
   double *qbar, *kbar, *vsum, *hbar, *mnorm;
   void *ws;
@@ -129,8 +144,11 @@ pisa_status_t pisa_select(const pisa_shape_t *shape, const pisa_stats_t *st, dou
  * costs about as much as dense attention. Any other value: PISA_EINVAL.
  * idx [B,H,n,topk] int32, each row ascending without
  * repeats, entries in [0, n) (any selection is accepted, e.g. one computed
- * elsewhere). Keys and values are read from the workspace copies written by
- * pisa_block_stats for the same q, k, v. o [B,H,L,D] receives the output in
+ * elsewhere; entries outside [0, n) are clamped into it, so they cannot read
+ * out of bounds). The call takes no k and v: keys, values, k̄, ΣV and H̄ are
+ * read from the copies that the last pisa_block_stats on st->ws wrote, so the
+ * result is attention over the k and v of that call (the library cannot
+ * check that they belong to this q). o, shaped like q, receives the output in
  * the I/O dtype (round to nearest even). */
 pisa_status_t pisa_attn_fwd(const pisa_shape_t *shape, const void *q, const pisa_stats_t *st,
                             int32_t first_order, const int32_t *idx, int32_t topk, double scale,

@@ -226,36 +226,6 @@ def head_forward(q, k, v, *, block: int, topk: int, scale: float, variant: str =
     return o, idx
 
 
-def pisa_attention(q, k, v, density: float, block_size: int = 64, sink_idx=None,
-                   variant: str = "hyd", cov_weight: float = 0.0, scale=None):
-    """[B, H, L, D] float64 entry with the README's keyword arguments."""
-    B, H, L, D = q.shape
-    s = 1.0 / math.sqrt(D) if scale is None else scale
-    n = num_blocks(L, block_size)
-    kk = topk_from_density(density, n)
-    o = np.empty_like(q)
-    idx = np.empty((B, H, n, kk), dtype=np.int64)
-    for b in range(B):
-        for h in range(H):
-            o[b, h], idx[b, h] = head_forward(q[b, h], k[b, h], v[b, h], block=block_size,
-                                              topk=kk, scale=s, variant=variant,
-                                              sink_idx=sink_idx, cov_weight=cov_weight)
-    return o, idx
-
-
-def dense_attention(q, k, v, scale=None, chunk: int = 1024):
-    """[B, H, L, D] float64 dense attention, query rows in chunks."""
-    B, H, L, D = q.shape
-    s = 1.0 / math.sqrt(D) if scale is None else scale
-    o = np.empty_like(q)
-    for b in range(B):
-        for h in range(H):
-            for lo in range(0, L, chunk):
-                r = slice(lo, min(L, lo + chunk))
-                o[b, h, r] = dense_rows(q[b, h], k[b, h], v[b, h], r, s)
-    return o
-
-
 def effective_flops(L: int, D: int, block: int, idx: np.ndarray, first_order: bool,
                     per_block: bool = False) -> float:
     """Credited FLOPs of the fused pass for one (batch, head): 4·D per exact
