@@ -197,6 +197,9 @@ def main():
     ap.add_argument("--pb1-reps", type=int, default=2,
                     help="calls of the per-block first-order variant timed on the same selection")
     ap.add_argument("--no-pb1", action="store_true")
+    ap.add_argument("--banded-reps", type=int, default=3,
+                    help="calls of the fused pass timed on a local (banded) selection of the same size")
+    ap.add_argument("--no-banded", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--sweep", action="store_true",
@@ -328,6 +331,31 @@ def main():
         print(f"[bench] pb1 {pms:.2f} ms, {pb1['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         del op
 
+    banded = None
+    if not args.no_banded:
+        # the same fused pass on a local selection: query block i takes the topk
+        # blocks nearest to it, as real DiT selections tend to be
+        start = np.clip(np.arange(n) - topk // 2, 0, n - topk)
+        bidx = np.broadcast_to(start[:, None] + np.arange(topk)[None, :], (w.B, w.H, n, topk))
+        bidx = torch.from_numpy(bidx.astype(np.int32).copy()).to(dev)
+        ob = torch.empty_like(qd)
+        bsa.attn_fwd(qd, st, bidx, s, hyd, out=ob)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.banded_reps):
+            bsa.attn_fwd(qd, st, bidx, s, hyd, out=ob)
+        e1.record()
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / args.banded_reps
+        fb = flops_from_idx(bidx.cpu().numpy(), w.L, w.D, w.block, hyd)
+        banded = {"selection": "banded (the topk blocks nearest each query block)", "ms": bms,
+                  "tflops": fb["total"] / (bms * 1e-3) / 1e12,
+                  "exact_phase_mfma_frac": fb["exact"] / (bms * 1e-3) / 1e12 / peak,
+                  "ms_vs_scattered": bms / ms["attn_fwd"]}
+        print(f"[bench] banded selection: fused {bms:.2f} ms", file=sys.stderr, flush=True)
+        del ob, bidx
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
@@ -360,6 +388,7 @@ def main():
                      "traffic": fused_traffic(w.name), "traffic_unit": "bytes per launch"},
         "dense": dense,
         "pb1": pb1,
+        "banded": banded,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

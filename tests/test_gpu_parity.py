@@ -394,11 +394,57 @@ def test_sweep_points_reduced_length(w):
     check_workload(w.replace(L=9450, H=2), qblock_sample=None)
 
 
-@pytest.mark.parametrize("blk,density,variant", [(128, 0.05, "hyd"), (64, 0.5, "0th")])
-def test_sweep_full_size_sampled(blk, density, variant):
-    w = synth.SWEEP_BASE.replace(block=blk, density=density, variant=variant,
-                                 name=f"sweep_full_b{blk}_d{density}_{variant}")
-    check_workload(w, heads=[(1, 5)], qblock_sample=6)
+@pytest.fixture(scope="module")
+def sweep_inputs():
+    """The Wan-shape sweep's inputs (B=2, H=40, L=75600, bf16), generated once
+    for all 20 full-size points."""
+    t0 = __import__("time").time()
+    qkv = synth.make_qkv(synth.SWEEP_BASE)
+    log(f"sweep inputs generated in {__import__('time').time() - t0:.1f}s")
+    return qkv
+
+
+@pytest.mark.parametrize("w", synth.sweep(), ids=lambda w: w.name)
+def test_sweep_full_size_sampled(w, sweep_inputs):
+    """Every block x density x variant point of the sweep at its full size
+    (B=2, H=40, L=75600), in the launch configuration the bench times: all 80
+    heads on the GPU; for head (1, 5) every selection row against the oracle
+    (tie rule) and the outputs of 6 query blocks, the first and the ragged
+    last among them, against the oracle with its own selection."""
+    check_workload(w, heads=[(1, 5)], qblock_sample=6, qkv=sweep_inputs)
+
+
+def banded_idx(B: int, H: int, n: int, topk: int) -> np.ndarray:
+    """A local selection: query block i takes the topk blocks nearest to it
+    (a window of consecutive blocks, clipped at the ends), ascending."""
+    start = np.clip(np.arange(n) - topk // 2, 0, n - topk)
+    rows = start[:, None] + np.arange(topk)[None, :]
+    return np.broadcast_to(rows, (B, H, n, topk)).astype(np.int32).copy()
+
+
+@pytest.mark.parametrize("w", [
+    W("banded_bf16_hyd", 1, 2, 5000, 128, 64, 0.15, "bf16", "hyd", None, 0.0, seed=91),
+    W("banded_bf16_blk128_0th_ragged", 1, 2, 5050, 128, 128, 0.2, "bf16", "0th", None, 0.0, seed=92),
+    W("banded_f32_d64", 1, 1, 3000, 64, 64, 0.1, "f32", "hyd", None, 0.0, seed=93),
+])
+def test_banded_selection_through_idx(w):
+    """A local (banded) selection fed through idx, the shape real DiT
+    selections take, compared in full with the oracle run on the same idx."""
+    q, k, v = synth.make_qkv(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (x.to(dev) for x in (q, k, v))
+    n = w.n_blocks
+    topk = bsa.topk_from_density(w.density, n)
+    idx = banded_idx(w.B, w.H, n, topk)
+    st = bsa.block_stats(qd, kd, vd, w.block)
+    o = bsa.attn_fwd(qd, st, torch.from_numpy(idx).to(dev), w.scale, w.variant)
+    torch.cuda.synchronize()
+    o = o.float().cpu().numpy()
+    for h in range(w.H):
+        qh, kh, vh = (synth.as_f64(x[0, h]) for x in (q, k, v))
+        ref, _ = oracle.head_forward(qh, kh, vh, block=w.block, topk=topk, scale=w.scale,
+                                     variant=w.variant, idx=idx[0, h])
+        compare_out(o[0, h], ref, w.dtype, f"{w.name} head {h} banded")
 
 
 def redo_count(st, w) -> int:
