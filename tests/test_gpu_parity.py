@@ -547,6 +547,12 @@ def test_bad_arguments_raise_before_launch():
         bsa.piecewise_sparse_attention_hyd(q, q, q, density=0.5)
     q = torch.zeros(1, 1, 100, 128, dtype=torch.bfloat16, device=dev)
     st = bsa.block_stats(q, q, q)
-    with pytest.raises(bsa.PisaError):
-        bsa.select(st, topk=3, scale=0.1)  # n = 2
+    with pytest.raises(ValueError):
+        bsa.select(st, topk=3, scale=0.1)  # n = 2: the binding refuses it before the call
+    idx = torch.zeros(1, 1, 2, 3, dtype=torch.int32, device=dev)
+    shape = bsa.make_shape(q, 64)
+    sst = st.struct()
+    # the library refuses it too, enqueueing nothing
+    assert bsa.load_library().pisa_select(bsa.ctypes.byref(shape), bsa.ctypes.byref(sst), 0.1, 0.0, 3,
+                                          bsa.PISA_SINK_NONE, idx.data_ptr(), None) == bsa.PISA_EINVAL
     torch.cuda.synchronize()
