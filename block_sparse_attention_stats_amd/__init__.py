@@ -27,12 +27,13 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libpisa.so")
 
-PISA_OK, PISA_EINVAL, PISA_ENOTSUP, PISA_EHIP = 0, 1, 2, 3
+PISA_OK, PISA_EINVAL, PISA_ENOTSUP, PISA_EHIP, PISA_ETOOBIG = 0, 1, 2, 3, 4
+NOALLOC_SCRATCH_BYTES = 256 << 20  # pisa.h PISA_NOALLOC_SCRATCH_BYTES
 PISA_F32, PISA_BF16 = 0, 1
 PISA_SINK_NONE = -(2 ** 31)
 EXPORTS = ("pisa_workspace_bytes", "pisa_block_stats", "pisa_select", "pisa_attn_fwd",
            "dense_workspace_bytes", "dense_attn_fwd", "pisa_status_string", "pisa_last_hip_error",
-           "pisa_block_stats_seg", "pisa_attn_fwd_seg", "dense_attn_fwd_seg")
+           "pisa_block_stats_seg", "pisa_attn_fwd_seg", "dense_attn_fwd_seg", "pisa_attn_fwd_noalloc")
 
 
 class PisaError(RuntimeError):
@@ -88,6 +89,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pisa_block_stats_seg": (I32, [SP, P, P, P, SG, STP, P]),
         "pisa_attn_fwd_seg": (I32, [SP, P, STP, I32, P, I32, D64, P, SG, P]),
         "dense_attn_fwd_seg": (I32, [SP, P, P, P, SG, D64, P, P, SZ, P]),
+        "pisa_attn_fwd_noalloc": (I32, [SP, P, P, P, I32, P, I32, D64, P, P]),
         "pisa_status_string": (ctypes.c_char_p, [I32]),
         "pisa_last_hip_error": (ctypes.c_char_p, []),
     }
@@ -102,7 +104,8 @@ def _status_text(status: int) -> str:
     try:
         return load_library().pisa_status_string(status).decode()
     except Exception:  # library missing: describe the code ourselves
-        return {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP runtime error"}.get(status, "?")
+        return {0: "ok", 1: "invalid argument", 2: "unsupported", 3: "HIP runtime error",
+                4: "problem larger than the fixed scratch"}.get(status, "?")
 
 
 def _check(status: int, where: str):
@@ -349,6 +352,27 @@ def attn_fwd(q, st: Stats, idx: torch.Tensor, scale: float, first_order=True,
     _check(load_library().pisa_attn_fwd(ctypes.byref(shape), q.data_ptr(), ctypes.byref(sst),
                                         code, idx.data_ptr(), topk,
                                         float(scale), o.data_ptr(), _stream()), "pisa_attn_fwd")
+    return o
+
+
+def attn_fwd_noalloc(q, k, v, idx: torch.Tensor, scale: float, first_order=True, block_size: int = 64,
+                     out: torch.Tensor | None = None, layout: str = "BHLD") -> torch.Tensor:
+    """Statistics and fused pass in one call of pisa_attn_fwd_noalloc, which
+    allocates no device memory and takes no workspace (its intermediates live
+    in a fixed per-device array of NOALLOC_SCRATCH_BYTES). The caller passes the
+    selection idx [B,H,n,topk] and may pass the output; a call whose shape
+    needs more scratch raises PisaError (PISA_ETOOBIG)."""
+    code = _variant_code(first_order)
+    _check_qkv(q, k, v)
+    shape = make_shape(q, block_size, layout)
+    topk = _check_idx(idx, shape)
+    if out is not None:
+        _check_io(out, shape, "out")
+    _on_gpu(q, k, v, idx, *(() if out is None else (out,)))
+    o = out if out is not None else torch.empty_like(q)
+    _check(load_library().pisa_attn_fwd_noalloc(ctypes.byref(shape), q.data_ptr(), k.data_ptr(),
+                                                v.data_ptr(), code, idx.data_ptr(), topk, float(scale),
+                                                o.data_ptr(), _stream()), "pisa_attn_fwd_noalloc")
     return o
 
 

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/pisa.h"
 #include "pisa_internal.h"
 
@@ -195,6 +197,77 @@ pisa::FwdArgs fwd_args(const pisa_shape_t* s, const pisa::WsLayout& w, const voi
   return a;
 }
 
+// Enqueues the statistics pass (arguments already validated).
+pisa_status_t run_stats(const pisa_shape_t* shape, const pisa::WsLayout& w, const void* q,
+                        const void* k, const void* v, const pisa_segments_t* seg,
+                        const pisa_stats_t* st, hipStream_t s) {
+  pisa_status_t rc;
+  pisa::StatsArgs a = stats_args(shape, w, q, k, v, seg, st, st->ws);
+  if ((rc = hip_status(pisa::launch_block_stats(shape->dtype, shape->D, pisa::kStatsFull, a, w.bh, s))))
+    return rc;
+  if ((rc = hip_status(pisa::launch_hbar_reduce(shape->dtype, shape->D, a, w.bh, s)))) return rc;
+  if (st->mnorm != nullptr)
+    if ((rc = hip_status(pisa::launch_block_stats(shape->dtype, shape->D, pisa::kStatsMnorm, a, w.bh, s))))
+      return rc;
+  return PISA_OK;
+}
+
+// The checks pisa_attn_fwd and its variants share.
+pisa_status_t check_fwd_args(const pisa::WsLayout& w, const void* q, const void* o,
+                             int32_t first_order, const int32_t* idx, int32_t topk, double scale) {
+  if (!tensor_ok(q) || !tensor_ok(o)) return PISA_EINVAL;
+  if (!(scale > 0.0) || !isfinite(scale)) return PISA_EINVAL;
+  if (first_order < 0 || first_order > 2) return PISA_EINVAL;
+  if (topk < 1 || topk > w.n) return PISA_EINVAL;
+  if (idx == nullptr || !aligned(idx, 4)) return PISA_EINVAL;
+  return PISA_OK;
+}
+
+// ---- pisa_attn_fwd_noalloc: every intermediate in one fixed array per
+// device. Host code never passes the array's own name to a kernel: its device
+// address is looked up once per device and kept.
+constexpr size_t kScratchBytes = PISA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+pisa_status_t scratch_on_current_device(uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return PISA_ENOTSUP;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr || !aligned(p, 256)) return PISA_EHIP;
+    g_scratch_ptr[dev] = (uint8_t*)p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PISA_OK;
+}
+
+// Where the statistics sit in the scratch array: after the workspace regions
+// the statistics pass and the fused pass use (the routing scores, the last
+// region, are not needed).
+struct NoAllocLayout {
+  size_t qbar, kbar, vsum, hbar, total;
+};
+
+NoAllocLayout noalloc_layout(const pisa_shape_t* s, const pisa::WsLayout& w) {
+  NoAllocLayout n;
+  const size_t rows = (size_t)w.bh * w.n * s->D * sizeof(double);
+  n.qbar = align256(w.scores);
+  n.kbar = align256(n.qbar + rows);
+  n.vsum = align256(n.kbar + rows);
+  n.hbar = align256(n.vsum + rows);
+  n.total = align256(n.hbar + (size_t)w.bh * s->D * s->D * sizeof(double));
+  return n;
+}
+
 }  // namespace
 
 PISA_API size_t pisa_workspace_bytes(const pisa_shape_t* shape) {
@@ -217,15 +290,7 @@ PISA_API pisa_status_t pisa_block_stats_seg(const pisa_shape_t* shape, const voi
   if (!tensor_ok(q) || !tensor_ok(k) || !tensor_ok(v)) return PISA_EINVAL;
   if ((rc = check_seg(shape, seg, true, false)) != PISA_OK) return rc;
   if ((rc = check_stats(st, w, false)) != PISA_OK) return rc;
-  hipStream_t s = (hipStream_t)stream;
-  pisa::StatsArgs a = stats_args(shape, w, q, k, v, seg, st, st->ws);
-  if ((rc = hip_status(pisa::launch_block_stats(shape->dtype, shape->D, pisa::kStatsFull, a, w.bh, s))))
-    return rc;
-  if ((rc = hip_status(pisa::launch_hbar_reduce(shape->dtype, shape->D, a, w.bh, s)))) return rc;
-  if (st->mnorm != nullptr)
-    if ((rc = hip_status(pisa::launch_block_stats(shape->dtype, shape->D, pisa::kStatsMnorm, a, w.bh, s))))
-      return rc;
-  return PISA_OK;
+  return run_stats(shape, w, q, k, v, seg, st, (hipStream_t)stream);
 }
 
 PISA_API pisa_status_t pisa_block_stats(const pisa_shape_t* shape, const void* q, const void* k,
@@ -273,12 +338,8 @@ PISA_API pisa_status_t pisa_attn_fwd_seg(const pisa_shape_t* shape, const void* 
   pisa::WsLayout w;
   pisa_status_t rc = check_shape(shape, &w);
   if (rc != PISA_OK) return rc;
-  if (!tensor_ok(q) || !tensor_ok(o)) return PISA_EINVAL;
+  if ((rc = check_fwd_args(w, q, o, first_order, idx, topk, scale)) != PISA_OK) return rc;
   if ((rc = check_seg(shape, seg, false, true)) != PISA_OK) return rc;
-  if (!(scale > 0.0) || !isfinite(scale)) return PISA_EINVAL;
-  if (first_order < 0 || first_order > 2) return PISA_EINVAL;
-  if (topk < 1 || topk > w.n) return PISA_EINVAL;
-  if (idx == nullptr || !aligned(idx, 4)) return PISA_EINVAL;
   if ((rc = check_stats(st, w, false)) != PISA_OK) return rc;
   pisa::FwdArgs a = fwd_args(shape, w, q, o, seg, st->ws, idx, topk, scale, first_order, 1);
   return hip_status(pisa::launch_fwd(shape->dtype, shape->D, a, (hipStream_t)stream));
@@ -289,6 +350,33 @@ PISA_API pisa_status_t pisa_attn_fwd(const pisa_shape_t* shape, const void* q,
                                      const int32_t* idx, int32_t topk, double scale, void* o,
                                      void* stream) {
   return pisa_attn_fwd_seg(shape, q, st, first_order, idx, topk, scale, o, nullptr, stream);
+}
+
+PISA_API pisa_status_t pisa_attn_fwd_noalloc(const pisa_shape_t* shape, const void* q,
+                                             const void* k, const void* v, int32_t first_order,
+                                             const int32_t* idx, int32_t topk, double scale,
+                                             void* o, void* stream) {
+  pisa::WsLayout w;
+  pisa_status_t rc = check_shape(shape, &w);
+  if (rc != PISA_OK) return rc;
+  if (!tensor_ok(k) || !tensor_ok(v)) return PISA_EINVAL;
+  if ((rc = check_fwd_args(w, q, o, first_order, idx, topk, scale)) != PISA_OK) return rc;
+  const NoAllocLayout nl = noalloc_layout(shape, w);
+  if (nl.total > kScratchBytes) return PISA_ETOOBIG;
+  uint8_t* base = nullptr;
+  if ((rc = scratch_on_current_device(&base)) != PISA_OK) return rc;
+  pisa_stats_t st;
+  st.qbar = (double*)(base + nl.qbar);
+  st.kbar = (double*)(base + nl.kbar);
+  st.vsum = (double*)(base + nl.vsum);
+  st.hbar = (double*)(base + nl.hbar);
+  st.mnorm = nullptr;
+  st.ws = base;
+  st.ws_bytes = nl.total;
+  hipStream_t s = (hipStream_t)stream;
+  if ((rc = run_stats(shape, w, q, k, v, nullptr, &st, s)) != PISA_OK) return rc;
+  pisa::FwdArgs a = fwd_args(shape, w, q, o, nullptr, base, idx, topk, scale, first_order, 1);
+  return hip_status(pisa::launch_fwd(shape->dtype, shape->D, a, s));
 }
 
 PISA_API pisa_status_t dense_attn_fwd_seg(const pisa_shape_t* shape, const void* q, const void* k,
@@ -321,6 +409,7 @@ PISA_API const char* pisa_status_string(pisa_status_t status) {
     case PISA_EINVAL: return "invalid argument";
     case PISA_ENOTSUP: return "unsupported shape or dtype";
     case PISA_EHIP: return "HIP runtime error";
+    case PISA_ETOOBIG: return "problem larger than the fixed scratch of pisa_attn_fwd_noalloc";
   }
   return "unknown status";
 }

@@ -25,16 +25,19 @@
  *    n_last = L - (n-1)*block tokens.
  *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
  *    and runs asynchronously; the caller keeps every buffer alive until the
- *    stream has passed the call. No entry point synchronises the device, and
- *    the library allocates no device memory: scratch space is the caller's
- *    workspace.
+ *    stream has passed the call. No entry point synchronises the device or
+ *    allocates device memory: scratch space is the caller's workspace, or for
+ *    pisa_attn_fwd_noalloc a fixed array that is part of the library's code
+ *    object on each device.
  *  - Arguments are validated before anything is enqueued. A bad argument
  *    returns PISA_EINVAL and enqueues nothing; a combination the library does
  *    not build returns PISA_ENOTSUP; a launch failure reported by the HIP
  *    runtime returns PISA_EHIP. No call aborts the process or throws.
- *  - The only state the library keeps is a per-host-thread copy of the text
- *    of the last HIP error (pisa_last_hip_error). Calls from several host
- *    threads at once are safe as long as they use different workspaces.
+ *  - The state the library keeps: a per-host-thread copy of the text of the
+ *    last HIP error (pisa_last_hip_error), and for pisa_attn_fwd_noalloc one
+ *    fixed scratch array per device. Calls from several host threads at once
+ *    are safe as long as they use different workspaces (and, for
+ *    pisa_attn_fwd_noalloc, different devices).
  */
 #ifndef PISA_H_
 #define PISA_H_
@@ -50,7 +53,8 @@ typedef enum {
   PISA_OK = 0,
   PISA_EINVAL = 1,  /* invalid argument; nothing enqueued */
   PISA_ENOTSUP = 2, /* valid but not built (e.g. an unsupported head_dim) */
-  PISA_EHIP = 3     /* the HIP runtime reported a launch error */
+  PISA_EHIP = 3,    /* the HIP runtime reported a launch error */
+  PISA_ETOOBIG = 4  /* pisa_attn_fwd_noalloc: the problem needs more than its fixed scratch */
 } pisa_status_t;
 
 typedef enum { PISA_F32 = 0, PISA_BF16 = 1 } pisa_dtype_t;
@@ -153,6 +157,28 @@ pisa_status_t pisa_select(const pisa_shape_t *shape, const pisa_stats_t *st, dou
 pisa_status_t pisa_attn_fwd(const pisa_shape_t *shape, const void *q, const pisa_stats_t *st,
                             int32_t first_order, const int32_t *idx, int32_t topk, double scale,
                             void *o, void *stream);
+
+/* pisa_block_stats followed by pisa_attn_fwd in one call that allocates
+ * nothing and takes no workspace, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Every intermediate (the operand copies of K and V, the
+ * block statistics, the partial sums and the counters) lives in one fixed
+ * array of PISA_NOALLOC_SCRATCH_BYTES per device, which the library holds
+ * from its first call on that device until the process ends; the caller
+ * passes only q, k, v, the selection and the output, with the meanings and
+ * layouts of pisa_block_stats and pisa_attn_fwd (one tensor per sequence,
+ * no covariance norm). The output equals that of pisa_block_stats +
+ * pisa_attn_fwd on the same arguments bit for bit.
+ * Returns PISA_ETOOBIG, enqueueing nothing, when the shape needs more
+ * scratch than that (about B*H*L*D*2*esz bytes of operand copies plus the
+ * statistics: FLUX-sized calls fit, a Wan-sized call does not). Every call on
+ * one device shares its array, and each call resets what must start at zero:
+ * calls that overlap on one device (on different streams, or from several
+ * host threads) race and give undefined results; order them on one stream. */
+#define PISA_NOALLOC_SCRATCH_BYTES ((size_t)256 << 20)
+pisa_status_t pisa_attn_fwd_noalloc(const pisa_shape_t *shape, const void *q, const void *k,
+                                    const void *v, int32_t first_order, const int32_t *idx,
+                                    int32_t topk, double scale, void *o, void *stream);
 
 /* Same-device dense baseline: o = softmax(scale * Q Kᵀ) V per (batch, head)
  * (the skill page's compute_exact_attention, used as the definition of dense

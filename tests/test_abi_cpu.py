@@ -57,7 +57,7 @@ def test_workspace_sizes():
 
 def test_status_strings():
     lib = bsa.load_library()
-    for code in range(4):
+    for code in range(5):
         assert lib.pisa_status_string(code).decode()
     assert lib.pisa_last_hip_error().decode() == ""
 
@@ -144,3 +144,23 @@ def test_segment_arguments_rejected():
     assert fwd(seg(o1=None)) == E
     assert dense(seg(k1=None)) == E and dense(seg(o1=None)) == E
 
+
+
+def test_noalloc_arguments_rejected_on_the_host():
+    """pisa_attn_fwd_noalloc validates like pisa_attn_fwd and refuses, before
+    touching the device, a shape whose intermediates exceed its fixed scratch."""
+    lib = bsa.load_library()
+    E = bsa.PISA_EINVAL
+    s = shape()  # n = 16, fits
+
+    def call(s=s, q=FAKE, k=FAKE, v=FAKE, fo=1, idx=FAKE, kk=2, scale=0.1, o=FAKE):
+        return lib.pisa_attn_fwd_noalloc(ctypes.byref(s), q, k, v, fo, idx, kk, scale, o, None)
+
+    assert call(k=None) == E and call(v=FAKE + 4) == E and call(q=None) == E and call(o=None) == E
+    assert call(fo=3) == E and call(kk=0) == E and call(kk=17) == E and call(idx=None) == E
+    assert call(scale=0.0) == E
+    assert call(s=shape(D=96)) == bsa.PISA_ENOTSUP
+    # K and V copies alone: 2 * 8 * 75600 * 128 * 2 bytes > 256 MiB
+    assert call(s=shape(H=8, L=75600)) == bsa.PISA_ETOOBIG
+    assert call(s=shape(H=40, L=75600)) == bsa.PISA_ETOOBIG
+    assert lib.pisa_status_string(bsa.PISA_ETOOBIG).decode().startswith("problem larger")
