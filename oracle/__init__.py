@@ -41,7 +41,8 @@ Readings where the pages are silent or garbled (each is listed in the design doc):
   * equal scores: lower block index wins;
   * the sink takes one of the k slots (score +inf); −1 names block n−1;
   * covariance routing is additive, score = s·q̄_i·k̄_j + λ·M_j, with the Frobenius
-    norm for M_j.
+    norm for M_j by default and the spectral norm as the option the gist's
+    "‖·‖_2" names.
 The last three points and the floor rule are parity unpinned by the pages: the
 tests check the oracle's internal consistency for them, nothing more.
 """
@@ -104,10 +105,17 @@ def block_stats(q: np.ndarray, k: np.ndarray, v: np.ndarray, block: int) -> dict
     return dict(qbar=qbar, kbar=kbar, vsum=vsum, H=H, Hbar=Hbar, sizes=sizes)
 
 
-def cov_norm(H: np.ndarray, Hbar: np.ndarray) -> np.ndarray:
-    """M_j = ‖H_j − H̄‖ (gist, "Covariance-Aware Routing"), Frobenius norm."""
+def cov_norm(H: np.ndarray, Hbar: np.ndarray, ord: str = "fro") -> np.ndarray:
+    """M_j = ‖H_j − H̄‖ (gist, "Covariance-Aware Routing"). ``ord="fro"``: the
+    Frobenius norm, sqrt of the sum of squares (the skill page's
+    score_attention_blocks takes a Frobenius norm); ``ord="spectral"``: the
+    2-norm the gist prints, the largest singular value (LAPACK's SVD)."""
     d = H - Hbar[None]
-    return np.sqrt((d * d).sum(axis=(1, 2)))
+    if ord == "fro":
+        return np.sqrt((d * d).sum(axis=(1, 2)))
+    if ord == "spectral":
+        return np.linalg.norm(d, ord=2, axis=(1, 2))
+    raise ValueError("ord must be 'fro' or 'spectral'")
 
 
 def sink_block(sink_idx, n: int):
@@ -199,7 +207,7 @@ def dense_rows(q, k, v, rows: slice, scale: float) -> np.ndarray:
 
 def head_forward(q, k, v, *, block: int, topk: int, scale: float, variant: str = "hyd",
                  sink_idx=None, cov_weight: float = 0.0, idx=None, qblocks=None,
-                 want_stats: bool = False):
+                 want_stats: bool = False, cov_ord: str = "fro"):
     """Whole forward pass for one (batch, head).
 
     q, k, v [L, D] float64. ``idx`` overrides the selection; ``qblocks`` limits
@@ -211,7 +219,7 @@ def head_forward(q, k, v, *, block: int, topk: int, scale: float, variant: str =
     L, D = q.shape
     st = block_stats(q, k, v, block)
     n = st["kbar"].shape[0]
-    M = cov_norm(st["H"], st["Hbar"]) if cov_weight else None
+    M = cov_norm(st["H"], st["Hbar"], cov_ord) if cov_weight else None
     st["M"] = M
     S = pooled_scores(st["qbar"], st["kbar"], scale, M, cov_weight, sink_idx)
     if idx is None:

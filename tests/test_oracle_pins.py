@@ -429,3 +429,58 @@ def test_effective_flops_counts():
     exp = 64 * (4 * D * 64 + 4 * D * 2) + 64 * (4 * D * 2 + 4 * D * 2) + 2 * (4 * D * 64 + 4 * D * 2)
     exp += 2 * D * D * (64 + 64 + 2)
     assert f == exp
+
+
+# ------------------------------------------------- spectral covariance norm
+def test_cov_norm_spectral_worked_example(golden):
+    """The two-block example with the 2-norm the gist's "Covariance-Aware
+    Routing" prints: H_0 − H̄ = [[5/4, −1/4], [3/4, 1/4]] and H_1 − H̄ its
+    negative. For a 2 x 2 matrix A, σ_max² = (tr AᵀA + sqrt(tr² − 4 det(A)²)) / 2;
+    here tr AᵀA = 9/4 and det A = 1/2, so M_0 = M_1 = sqrt((9 + √65) / 8)."""
+    g = golden
+    q, k, v = (np.array(g["inputs"][x], dtype=np.float64) for x in "qkv")
+    st = oracle.block_stats(q, k, v, 2)
+    M = oracle.cov_norm(st["H"], st["Hbar"], "spectral")
+    want = math.sqrt((9.0 + math.sqrt(65.0)) / 8.0)
+    np.testing.assert_allclose(M, [want, want], rtol=1e-15, atol=0)
+    assert (M < oracle.cov_norm(st["H"], st["Hbar"], "fro")).all()  # rank 2: strictly below Frobenius
+
+
+def test_cov_norm_spectral_closed_forms():
+    """Diagonal: the largest |entry|. Rank one u vᵀ: ‖u‖·‖v‖ (and equal to the
+    Frobenius norm). A block diagonal of rotations times scales: the largest
+    scale. Hbar is zero in each case, so M_j is the norm of H_j itself."""
+    D = 6
+    rng = np.random.default_rng(5)
+    u, w = rng.normal(size=D), rng.normal(size=D)
+    c, s = math.cos(0.7), math.sin(0.7)
+    rot = np.eye(D)
+    rot[:2, :2] = [[3 * c, -3 * s], [3 * s, 3 * c]]  # scale 3 rotation in the first plane
+    rot[2, 2], rot[3, 3], rot[4, 4], rot[5, 5] = 0.5, -1.5, 2.0, 0.0
+    H = np.stack([np.diag([3.0, -4.0, 1.0, 0.0, 2.5, -0.5]), np.outer(u, w), rot])
+    M = oracle.cov_norm(H, np.zeros((D, D)), "spectral")
+    np.testing.assert_allclose(M, [4.0, np.linalg.norm(u) * np.linalg.norm(w), 3.0], rtol=1e-14)
+    np.testing.assert_allclose(M[1], oracle.cov_norm(H, np.zeros((D, D)), "fro")[1], rtol=1e-14)
+
+
+def test_cov_norm_spectral_power_iteration_and_bounds():
+    """On random matrices: the power iteration on AᵀA (well separated top
+    singular value by construction) reaches the same value, and
+    ‖A‖_2 ≤ ‖A‖_F ≤ sqrt(rank)·‖A‖_2."""
+    D, n = 16, 5
+    rng = np.random.default_rng(9)
+    H = rng.normal(size=(n, D, D))
+    H[:, 0, :] *= 8.0  # one dominant row direction: a clear gap
+    Hbar = H.mean(axis=0)
+    M2 = oracle.cov_norm(H, Hbar, "spectral")
+    MF = oracle.cov_norm(H, Hbar, "fro")
+    for j in range(n):
+        A = H[j] - Hbar
+        x = np.ones(D)
+        for _ in range(500):
+            x = A.T @ (A @ x)
+            x /= np.sqrt(x @ x)
+        np.testing.assert_allclose(np.sqrt(x @ (A.T @ (A @ x))), M2[j], rtol=1e-12)
+    assert (M2 <= MF * (1 + 1e-15)).all() and (MF <= math.sqrt(D) * M2 * (1 + 1e-15)).all()
+    with pytest.raises(ValueError):
+        oracle.cov_norm(H, Hbar, "nuclear")
