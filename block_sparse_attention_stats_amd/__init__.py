@@ -62,7 +62,17 @@ class Segments(ctypes.Structure):
 class StatsStruct(ctypes.Structure):
     _fields_ = [("qbar", ctypes.c_void_p), ("kbar", ctypes.c_void_p), ("vsum", ctypes.c_void_p),
                 ("hbar", ctypes.c_void_p), ("mnorm", ctypes.c_void_p), ("ws", ctypes.c_void_p),
-                ("ws_bytes", ctypes.c_size_t)]
+                ("ws_bytes", ctypes.c_size_t), ("mnorm_ord", ctypes.c_int32)]
+
+
+# norm of M_j = ||H_j - H-bar|| (pisa.h PISA_NORM_*)
+NORMS = {"fro": 0, "spectral": 2}
+
+
+def _norm_code(cov_norm: str) -> int:
+    if cov_norm not in NORMS:
+        raise ValueError(f"unknown cov_norm {cov_norm!r}; expected one of {sorted(NORMS)}")
+    return NORMS[cov_norm]
 
 
 _lib_handle = None
@@ -219,6 +229,7 @@ class Stats:
     hbar: torch.Tensor   # [B,H,D,D] fp64
     mnorm: torch.Tensor | None  # [B,H,n] fp64
     ws: torch.Tensor     # uint8 workspace
+    mnorm_ord: str = "fro"  # norm of M_j: "fro" or "spectral"
 
     def check(self, shape: Shape | None = None):
         """Every buffer has the size and dtype that the shape (default: its
@@ -247,7 +258,7 @@ class Stats:
     def struct(self) -> StatsStruct:
         return StatsStruct(self.qbar.data_ptr(), self.kbar.data_ptr(), self.vsum.data_ptr(),
                            self.hbar.data_ptr(), self.mnorm.data_ptr() if self.mnorm is not None else None,
-                           self.ws.data_ptr(), self.ws.numel())
+                           self.ws.data_ptr(), self.ws.numel(), _norm_code(self.mnorm_ord))
 
 
 def _shape_tuple(shape: Shape) -> tuple:
@@ -272,10 +283,12 @@ def alloc_stats(shape: Shape, device, want_mnorm: bool) -> Stats:
 
 
 def block_stats(q, k, v, block_size: int = 64, want_mnorm: bool = False, out: Stats | None = None,
-                layout: str = "BHLD") -> Stats:
+                layout: str = "BHLD", cov_norm: str = "fro") -> Stats:
     """Step 1: q̄, k̄, ΣV, H̄ (and M_j when ``want_mnorm``) via pisa_block_stats.
     ``layout`` is that of q, k, v (and of the output of attn_fwd with these
-    statistics); the statistics themselves are [B,H,...] either way."""
+    statistics); the statistics themselves are [B,H,...] either way.
+    ``cov_norm``: the norm of M_j, "fro" (Frobenius) or "spectral" (2-norm)."""
+    _norm_code(cov_norm)
     _check_qkv(q, k, v)
     shape = make_shape(q, block_size, layout)
     if out is not None:
@@ -284,6 +297,7 @@ def block_stats(q, k, v, block_size: int = 64, want_mnorm: bool = False, out: St
             raise ValueError("want_mnorm needs Stats.mnorm")
     _on_gpu(q, k, v, *(() if out is None else out.tensors()))
     st = out if out is not None else alloc_stats(shape, q.device, want_mnorm)
+    st.mnorm_ord = cov_norm
     sst = st.struct()
     _check(load_library().pisa_block_stats(ctypes.byref(shape), q.data_ptr(), k.data_ptr(),
                                            v.data_ptr(), ctypes.byref(sst), _stream()),
@@ -403,7 +417,7 @@ def dense(q, k, v, scale: float | None = None, out: torch.Tensor | None = None,
 def piecewise_sparse_attention_hyd(q, k, v, density: float = 0.15, block_size: int = 64,
                                    sink_idx=None, cov_weight: float = 0.0, scale=None,
                                    first_order=True, return_idx: bool = False,
-                                   layout: str = "BHLD"):
+                                   layout: str = "BHLD", cov_norm: str = "fro"):
     """PISA forward (hybrid order: zeroth order + global first-order correction).
     q, k, v (and the output) are [B,H,L,D], or [B,L,H,D] with layout="BLHD"."""
     _check_qkv(q, k, v)
@@ -412,7 +426,7 @@ def piecewise_sparse_attention_hyd(q, k, v, density: float = 0.15, block_size: i
     s = 1.0 / math.sqrt(D) if scale is None else float(scale)
     n = num_blocks(L, block_size)
     topk = topk_from_density(density, n)
-    st = block_stats(q, k, v, block_size, want_mnorm=cov_weight > 0, layout=layout)
+    st = block_stats(q, k, v, block_size, want_mnorm=cov_weight > 0, layout=layout, cov_norm=cov_norm)
     idx = select(st, topk, s, cov_weight, sink_idx)
     o = attn_fwd(q, st, idx, s, first_order)
     return (o, idx) if return_idx else o
@@ -420,19 +434,21 @@ def piecewise_sparse_attention_hyd(q, k, v, density: float = 0.15, block_size: i
 
 def piecewise_sparse_attention_0th(q, k, v, density: float = 0.15, block_size: int = 64,
                                    sink_idx=None, cov_weight: float = 0.0, scale=None,
-                                   return_idx: bool = False, layout: str = "BHLD"):
+                                   return_idx: bool = False, layout: str = "BHLD", cov_norm: str = "fro"):
     """PISA forward, zeroth-order-only variant (no global first-order term)."""
     return piecewise_sparse_attention_hyd(q, k, v, density, block_size, sink_idx, cov_weight, scale,
-                                          first_order=False, return_idx=return_idx, layout=layout)
+                                          first_order=False, return_idx=return_idx, layout=layout,
+                                          cov_norm=cov_norm)
 
 
 def piecewise_sparse_attention_pb1(q, k, v, density: float = 0.15, block_size: int = 64,
                                    sink_idx=None, cov_weight: float = 0.0, scale=None,
-                                   return_idx: bool = False, layout: str = "BHLD"):
+                                   return_idx: bool = False, layout: str = "BHLD", cov_norm: str = "fro"):
     """PISA forward with a first-order term per unselected block (q·H_j for each
     block instead of the global H̄); costs about as much as dense attention."""
     return piecewise_sparse_attention_hyd(q, k, v, density, block_size, sink_idx, cov_weight, scale,
-                                          first_order="pb1", return_idx=return_idx, layout=layout)
+                                          first_order="pb1", return_idx=return_idx, layout=layout,
+                                          cov_norm=cov_norm)
 
 
 piecewise_sparse_attention = piecewise_sparse_attention_hyd
@@ -457,7 +473,7 @@ def _segments(L0: int, q1, k1=None, v1=None, o1=None) -> Segments:
 
 
 def block_stats_seg(q0, k0, v0, q1, k1, v1, block_size: int = 64, want_mnorm: bool = False,
-                    out: Stats | None = None, layout: str = "BHLD") -> Stats:
+                    out: Stats | None = None, layout: str = "BHLD", cov_norm: str = "fro") -> Stats:
     """Step 1 on the sequence q0 ++ q1 (and k, v likewise), via pisa_block_stats_seg."""
     _check_qkv(q0, k0, v0)
     _check_qkv(q1, k1, v1)
@@ -467,8 +483,10 @@ def block_stats_seg(q0, k0, v0, q1, k1, v1, block_size: int = 64, want_mnorm: bo
         out.check(shape)
         if want_mnorm and out.mnorm is None:
             raise ValueError("want_mnorm needs Stats.mnorm")
+    _norm_code(cov_norm)
     _on_gpu(q0, k0, v0, q1, k1, v1, *(() if out is None else out.tensors()))
     st = out if out is not None else alloc_stats(shape, q0.device, want_mnorm)
+    st.mnorm_ord = cov_norm
     sst = st.struct()
     seg = _segments(L0, q1, k1, v1)
     _check(load_library().pisa_block_stats_seg(ctypes.byref(shape), q0.data_ptr(), k0.data_ptr(),
@@ -533,7 +551,7 @@ def dense_seg(q0, k0, v0, q1, k1, v1, scale: float | None = None, layout: str = 
 def mmdit_joint_attention(txt_q, txt_k, txt_v, img_q, img_k, img_v, density: float = 0.15,
                           block_size: int = 64, text_first: bool = True, variant="hyd",
                           cov_weight: float = 0.0, scale=None, layout: str = "BHLD",
-                          return_idx: bool = False):
+                          return_idx: bool = False, cov_norm: str = "fro"):
     """PISA over the joint text + image sequence of an MMDiT block, with the
     text block as the attention sink (README, "Attention sink for MMDiT"):
     text first (FLUX) forces block 0, text last (Hunyuan-Video) block n-1.
@@ -546,7 +564,8 @@ def mmdit_joint_attention(txt_q, txt_k, txt_v, img_q, img_k, img_v, density: flo
     shape = _joint_shape(q0, q1, block_size, layout)
     s = 1.0 / math.sqrt(shape.D) if scale is None else float(scale)
     topk = topk_from_density(density, num_blocks(shape.L, block_size))
-    st = block_stats_seg(q0, k0, v0, q1, k1, v1, block_size, want_mnorm=cov_weight > 0, layout=layout)
+    st = block_stats_seg(q0, k0, v0, q1, k1, v1, block_size, want_mnorm=cov_weight > 0, layout=layout,
+                         cov_norm=cov_norm)
     idx = select(st, topk, s, cov_weight, sink)
     o0, o1 = attn_fwd_seg(q0, q1, st, idx, s, variant)
     o_txt, o_img = (o0, o1) if text_first else (o1, o0)

@@ -78,6 +78,7 @@ pisa_status_t check_stats(const pisa_stats_t* st, const pisa::WsLayout& w, bool 
     if (x == nullptr || !aligned(x, 8)) return PISA_EINVAL;
   if (need_mnorm && st->mnorm == nullptr) return PISA_EINVAL;
   if (st->mnorm != nullptr && !aligned(st->mnorm, 8)) return PISA_EINVAL;
+  if (st->mnorm_ord != PISA_NORM_FRO && st->mnorm_ord != PISA_NORM_SPECTRAL) return PISA_EINVAL;
   if (st->ws == nullptr || !aligned(st->ws, 256) || st->ws_bytes < w.total) return PISA_EINVAL;
   return PISA_OK;
 }
@@ -206,10 +207,10 @@ pisa_status_t run_stats(const pisa_shape_t* shape, const pisa::WsLayout& w, cons
   if ((rc = hip_status(pisa::launch_block_stats(shape->dtype, shape->D, pisa::kStatsFull, a, w.bh, s))))
     return rc;
   if ((rc = hip_status(pisa::launch_hbar_reduce(shape->dtype, shape->D, a, w.bh, s)))) return rc;
-  if (st->mnorm != nullptr)
-    if ((rc = hip_status(pisa::launch_block_stats(shape->dtype, shape->D, pisa::kStatsMnorm, a, w.bh, s))))
-      return rc;
-  return PISA_OK;
+  if (st->mnorm == nullptr) return PISA_OK;
+  if (st->mnorm_ord == PISA_NORM_SPECTRAL)
+    return hip_status(pisa::launch_mnorm_spectral(shape->dtype, shape->D, a, w.bh, s));
+  return hip_status(pisa::launch_block_stats(shape->dtype, shape->D, pisa::kStatsMnorm, a, w.bh, s));
 }
 
 // The checks pisa_attn_fwd and its variants share.
@@ -371,6 +372,7 @@ PISA_API pisa_status_t pisa_attn_fwd_noalloc(const pisa_shape_t* shape, const vo
   st.vsum = (double*)(base + nl.vsum);
   st.hbar = (double*)(base + nl.hbar);
   st.mnorm = nullptr;
+  st.mnorm_ord = PISA_NORM_FRO;
   st.ws = base;
   st.ws_bytes = nl.total;
   hipStream_t s = (hipStream_t)stream;

@@ -83,6 +83,8 @@ enum StatsMode { kStatsFull = 0, kStatsMnorm = 1, kStatsPackOnly = 2 };
 hipError_t launch_block_stats(int dtype, int D, int mode, const StatsArgs& a, long bh,
                               hipStream_t s);
 hipError_t launch_hbar_reduce(int dtype, int D, const StatsArgs& a, long bh, hipStream_t s);
+// M_j = ||H_j − H̄||_2 per block (after the statistics and H̄ are complete).
+hipError_t launch_mnorm_spectral(int dtype, int D, const StatsArgs& a, long bh, hipStream_t s);
 hipError_t launch_scores(int D, const ScoreArgs& a, long bh, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, long rows, hipStream_t s);
 // Fast pass, then the careful pass over the query tiles the fast pass queued.

@@ -88,8 +88,9 @@ typedef struct {
  *   kbar  [B,H,n,D] fp64  key centroid k̄_j (mean of the block's keys)
  *   vsum  [B,H,n,D] fp64  ΣV_j, the sum (not mean) of the block's values
  *   hbar  [B,H,D,D] fp64  H̄[d][e] = (1/n) Σ_j Σ_n (k_n - k̄_j)[d] v_n[e]
- *   mnorm [B,H,n]   fp64  M_j = ||H_j - H̄||_F; may be NULL unless the
- *                         covariance-aware routing of pisa_select is used
+ *   mnorm [B,H,n]   fp64  M_j = ||H_j - H̄|| in the norm mnorm_ord names
+ *                         (below); may be NULL unless the covariance-aware
+ *                         routing of pisa_select is used
  *   ws / ws_bytes         workspace of at least pisa_workspace_bytes(shape)
  *                         bytes, 256-byte aligned (see below).
  * Precision: q̄, k̄ and ΣV are fp64 sums of the inputs (exact for bf16),
@@ -97,9 +98,9 @@ typedef struct {
  * matrix cores: the products k[d]·v[e] are exact for bf16 inputs, each run of
  * consecutive blocks (up to 1024 tokens) is summed in one fp32 accumulator,
  * from which k̄_j[d]·ΣV_j[e] (rounded to fp32) is subtracted as block j ends,
- * and the runs are summed in fp64. M_j takes the block's fp32 sum of
- * products, subtracts k̄_j[d]·ΣV_j[e] and H̄ in fp64, and sums the squares in
- * fp64.
+ * and the runs are summed in fp64. The Frobenius M_j takes the block's fp32
+ * sum of products, subtracts k̄_j[d]·ΣV_j[e] and H̄ in fp64, and sums the
+ * squares in fp64; the spectral M_j sums the block's products in fp64.
  * The workspace: pisa_block_stats writes there the copies of K, V, k̄, ΣV and
  * H̄ in the I/O dtype, laid out in the operand order of the fused kernel, and
  * the largest key norms; pisa_select stages its routing scores there;
@@ -111,7 +112,22 @@ typedef struct {
   double *qbar, *kbar, *vsum, *hbar, *mnorm;
   void *ws;
   size_t ws_bytes;
+  int32_t mnorm_ord; /* PISA_NORM_FRO (0, a zeroed struct) or PISA_NORM_SPECTRAL */
 } pisa_stats_t;
+
+/* The norm of M_j = ||H_j - H̄||: Frobenius (the square root of the sum of
+ * squares, as the skill page's scoring code takes it), or spectral, the
+ * largest singular value (the 2-norm the gist's "Covariance-Aware Routing"
+ * writes). The spectral norm is found by a fixed number of fp64 steps per
+ * block, whatever the gap between the largest singular values: the Gram
+ * matrix (H_j - H̄)ᵀ(H_j - H̄) is formed in fp64 from the block's keys and
+ * values, reduced to tridiagonal form by Householder reflections and its
+ * largest eigenvalue found by Sturm-count bisection. It costs one workgroup
+ * of about D³ fp64 work per block, so it suits image-sized sequences (the
+ * pages apply covariance-aware routing to images). Any other value of
+ * mnorm_ord: PISA_EINVAL. */
+#define PISA_NORM_FRO 0
+#define PISA_NORM_SPECTRAL 2
 
 /* Bytes of workspace the stats / select / forward calls need for `shape`
  * (0 if the shape is invalid). */

@@ -48,6 +48,7 @@ class Workload:
     sink_idx: int | None = None  # None, 0 or -1
     cov_weight: float = 0.0  # weight of the covariance-norm term in routing
     seed: int = 0
+    cov_norm: str = "fro"  # norm of that term: "fro" (Frobenius) or "spectral" (2-norm)
 
     @property
     def n_blocks(self) -> int:

@@ -39,7 +39,8 @@ def gamma(m: int) -> float:
     return m * U32 / (1.0 - m * U32)
 
 
-def stats_bounds(k: np.ndarray, v: np.ndarray, st_ref: dict, block: int, dtype: str, want_m: bool):
+def stats_bounds(k: np.ndarray, v: np.ndarray, st_ref: dict, block: int, dtype: str, want_m: bool,
+                 cov_norm: str = "fro"):
     """Largest errors the library's arithmetic allows in H̄ (per element) and
     in M_j (per block), for one head's fp64 k, v [L, D].
 
@@ -51,9 +52,15 @@ def stats_bounds(k: np.ndarray, v: np.ndarray, st_ref: dict, block: int, dtype: 
     by n. Each run sums at most m = 1024 + 1024/block terms, so
         |ΔH̄_de| ≤ (1/n) [(γ_m + u_in) Σ_t |k_td||v_te| + (γ_m + 3u) Σ_j |k̄_jd||ΣV_je|]
     with u_in = u for fp32 inputs, else 0 (fp64 roundings are below 1e-15 of it).
-    M_j = ||H_j − H̄||_F is formed in fp64 from the block's G_j = Σ_t k_tᵀv_t,
-    accumulated in fp32 over its n_j tokens, minus k̄_jᵀΣV_j in fp64, minus
-    the H̄ above, so |ΔM_j| ≤ ||(γ_{n_j} + u_in) |K_j|ᵀ|V_j| ||_F + ||ΔH̄ bound||_F."""
+    The Frobenius M_j = ||H_j − H̄||_F is formed in fp64 from the block's
+    G_j = Σ_t k_tᵀv_t, accumulated in fp32 over its n_j tokens, minus
+    k̄_jᵀΣV_j in fp64, minus the H̄ above, so
+        |ΔM_j| ≤ ||(γ_{n_j} + u_in) |K_j|ᵀ|V_j| ||_F + ||ΔH̄ bound||_F.
+    The spectral M_j = ||H_j − H̄||_2 sums G_j in fp64 (exact products, n_j
+    terms: n_j·2^-53 relative) and finds the largest eigenvalue of the Gram
+    matrix by a backward-stable fp64 reduction, within 1e-12 relative here;
+    since | ||A||_2 − ||A'||_2 | ≤ ||A − A'||_2 ≤ ||A − A'||_F the same form of
+    bound holds."""
     n = st_ref["kbar"].shape[0]
     L = k.shape[0]
     u_in = U32 if dtype == "f32" else 0.0
@@ -68,8 +75,9 @@ def stats_bounds(k: np.ndarray, v: np.ndarray, st_ref: dict, block: int, dtype: 
     mb = np.empty(n)
     for j in range(n):
         lo, hi = j * block, min(L, (j + 1) * block)
-        g = (gamma(hi - lo) + u_in) * (ka[lo:hi].T @ va[lo:hi])
-        mb[j] = float(np.sqrt((g * g).sum())) + hb_f + 1e-12
+        c = gamma(hi - lo) + u_in if cov_norm == "fro" else 1.01 * (hi - lo) * 2.0 ** -53
+        g = c * (ka[lo:hi].T @ va[lo:hi])
+        mb[j] = float(np.sqrt((g * g).sum())) + hb_f + 1e-12 * (1.0 + float(st_ref["M"][j]))
     return hb, mb
 
 
@@ -116,7 +124,7 @@ def run_gpu(w: synth.Workload, q, k, v, oracle_idx=None):
     s = w.scale
     n = w.n_blocks
     topk = bsa.topk_from_density(w.density, n)
-    st = bsa.block_stats(q, k, v, w.block, want_mnorm=w.cov_weight > 0)
+    st = bsa.block_stats(q, k, v, w.block, want_mnorm=w.cov_weight > 0, cov_norm=w.cov_norm)
     idx = bsa.select(st, topk, s, w.cov_weight, w.sink_idx)
     o = bsa.attn_fwd(q, st, idx, s, w.variant)
     o_or = None
@@ -149,7 +157,8 @@ def check_workload(w: synth.Workload, heads=None, qblock_sample: int | None = No
         qbs = None if qblock_sample is None else sample_qblocks(n, qblock_sample, seed + 7 * h + b)
         o_ref, idx_ref, st_ref, S = oracle.head_forward(
             qh, kh, vh, block=w.block, topk=topk, scale=w.scale, variant=w.variant,
-            sink_idx=w.sink_idx, cov_weight=w.cov_weight, qblocks=qbs, want_stats=True)
+            sink_idx=w.sink_idx, cov_weight=w.cov_weight, qblocks=qbs, want_stats=True,
+            cov_ord=w.cov_norm)
         ora[(b, h)] = (o_ref, idx_ref, st_ref, S, qbs)
     idx_full = np.zeros((w.B, w.H, n, topk), dtype=np.int64)
     for (b, h), val in ora.items():
@@ -167,7 +176,7 @@ def check_workload(w: synth.Workload, heads=None, qblock_sample: int | None = No
         np.testing.assert_allclose(vsum[b, h], st_ref["vsum"], rtol=0, atol=1e-10)
         # H̄ and M_j: bounds derived from the library's arithmetic (stats_bounds)
         kh, vh = synth.as_f64(k[b, h]), synth.as_f64(v[b, h])
-        hb_bound, m_bound = stats_bounds(kh, vh, st_ref, w.block, w.dtype, mnorm is not None)
+        hb_bound, m_bound = stats_bounds(kh, vh, st_ref, w.block, w.dtype, mnorm is not None, w.cov_norm)
         err_h = np.abs(hbar[b, h] - st_ref["Hbar"])
         log(f"    head ({b},{h}) H-bar: max-abs {err_h.max():.3e}, largest share of its bound "
             f"{(err_h / hb_bound).max():.2e}")

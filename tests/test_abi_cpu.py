@@ -102,6 +102,10 @@ def test_bad_arguments_rejected():
     assert sel(st=st_mis) == E  # misaligned fp64 buffer
     st_ws = bsa.StatsStruct(FAKE, FAKE, FAKE, FAKE, None, FAKE + 16, 1 << 40)
     assert sel(st=st_ws) == E  # workspace not 256-aligned
+    for bad_ord in (1, 3, -1):  # the norm of M_j: only PISA_NORM_FRO (0) or PISA_NORM_SPECTRAL (2)
+        st_ord = bsa.StatsStruct(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, bad_ord)
+        assert sel(st=st_ord) == E
+        assert lib.pisa_block_stats(ctypes.byref(s), FAKE, FAKE, FAKE, ctypes.byref(st_ord), None) == E
     fwd = lambda q=FAKE, o=FAKE, fo=1, idx=FAKE, k=2, scale=0.1: lib.pisa_attn_fwd(
         ctypes.byref(s), q, ctypes.byref(st), fo, idx, k, scale, o, None)
     assert fwd(q=None) == E and fwd(q=FAKE + 8) == E and fwd(o=None) == E

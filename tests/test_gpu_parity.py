@@ -6,6 +6,7 @@ configuration as the bench and are compared on sampled heads and query blocks
 that the oracle evaluates one by one.
 """
 
+import math
 import os
 import subprocess
 
@@ -113,7 +114,9 @@ def test_per_block_first_order_careful_kernel(dtype):
     assert redo_count(res["stats"], w) == w.B * w.H * w.n_blocks
 
 
-LAYOUT_CASES = [SMALL[0], SMALL[3], SMALL[4], SMALL[5], SMALL[7], PB1[0], PB1[1]]
+LAYOUT_CASES = [SMALL[0], SMALL[3], SMALL[4], SMALL[5], SMALL[7], PB1[0], PB1[1],
+                W("layout_spectral", 1, 2, 1100, 64, 128, 0.2, "bf16", "0th", 0, 0.05, seed=77,
+                  cov_norm="spectral")]
 
 
 @pytest.mark.parametrize("w", LAYOUT_CASES, ids=lambda w: w.name)
@@ -130,14 +133,14 @@ def test_blhd_layout_matches_bhld(w):
     topk = bsa.topk_from_density(w.density, n)
     runs = []
     for (a, b, c, lay) in ((qd, kd, vd, "BHLD"), (qt, kt, vt, "BLHD")):
-        st = bsa.block_stats(a, b, c, w.block, want_mnorm=w.cov_weight > 0, layout=lay)
+        st = bsa.block_stats(a, b, c, w.block, want_mnorm=w.cov_weight > 0, layout=lay, cov_norm=w.cov_norm)
         idx = bsa.select(st, topk, w.scale, w.cov_weight, w.sink_idx)
         o = bsa.attn_fwd(a, st, idx, w.scale, w.variant)
         od = bsa.dense(a, b, c, w.scale, layout=lay)
         runs.append((st, idx, o, od))
     torch.cuda.synchronize()
     (s1, i1, o1, d1), (s2, i2, o2, d2) = runs
-    for name in ("qbar", "kbar", "vsum", "hbar"):
+    for name in ("qbar", "kbar", "vsum", "hbar") + (("mnorm",) if w.cov_weight > 0 else ()):
         assert torch.equal(getattr(s1, name), getattr(s2, name)), name
     assert torch.equal(i1, i2)
     assert o2.shape == (w.B, w.L, w.H, w.D)
@@ -227,6 +230,8 @@ JOINT_CASES = [
     (W("joint_text_last", 1, 2, 1256, 128, 64, 0.2, "bf16", "pb1", -1, 0.0, seed=72), 1000, "BLHD"),
     (W("joint_blk128_f32", 2, 1, 700, 64, 128, 0.3, "f32", "0th", None, 0.0, seed=73), 130, "BHLD"),
     (W("joint_one_token_first", 1, 2, 900, 128, 64, 0.25, "bf16", "hyd", 0, 0.0, seed=74), 1, "BLHD"),
+    (W("joint_spectral_text_last", 1, 2, 1256, 128, 64, 0.2, "bf16", "hyd", -1, 0.1, seed=76,
+       cov_norm="spectral"), 1000, "BLHD"),
 ]
 
 
@@ -245,11 +250,12 @@ def test_joint_sequence_matches_single_tensor(case):
     (q0, q1), (k0, k1), (v0, v1) = parts
     n = w.n_blocks
     topk = bsa.topk_from_density(w.density, n)
-    st = bsa.block_stats(*full, w.block, want_mnorm=w.cov_weight > 0, layout=layout)
+    st = bsa.block_stats(*full, w.block, want_mnorm=w.cov_weight > 0, layout=layout, cov_norm=w.cov_norm)
     idx = bsa.select(st, topk, w.scale, w.cov_weight, w.sink_idx)
     o = bsa.attn_fwd(full[0], st, idx, w.scale, w.variant)
     od = bsa.dense(*full, w.scale, layout=layout)
-    st2 = bsa.block_stats_seg(q0, k0, v0, q1, k1, v1, w.block, want_mnorm=w.cov_weight > 0, layout=layout)
+    st2 = bsa.block_stats_seg(q0, k0, v0, q1, k1, v1, w.block, want_mnorm=w.cov_weight > 0, layout=layout,
+                              cov_norm=w.cov_norm)
     idx2 = bsa.select(st2, topk, w.scale, w.cov_weight, w.sink_idx)
     o0, o1 = bsa.attn_fwd_seg(q0, q1, st2, idx2, w.scale, w.variant)
     d0, d1 = bsa.dense_seg(q0, k0, v0, q1, k1, v1, w.scale, layout=layout)
@@ -327,6 +333,64 @@ def test_plain_c_caller_matches_binding(w, tmp_path):
     np.testing.assert_array_equal(c_idx, idx.cpu().numpy())
     c_o = np.fromfile(str(tmp_path / "o.bin"), dtype=np.int16 if w.dtype == "bf16" else np.float32)
     np.testing.assert_array_equal(c_o.reshape(o.shape), raw(o.cpu()).numpy())
+
+
+# covariance routing with the spectral norm of H_j − H̄ (the gist's 2-norm)
+SPECTRAL = [
+    W("spec_bf16_cov", 1, 2, 1200, 128, 64, 0.15, "bf16", "hyd", 0, 0.1, seed=201, cov_norm="spectral"),
+    W("spec_bf16_balanced", 1, 2, 1200, 128, 64, 0.15, "bf16", "hyd", None, 1e-3, seed=202,
+      cov_norm="spectral"),
+    W("spec_f32_d64_blk128_ragged", 1, 2, 1000, 64, 128, 0.2, "f32", "0th", -1, 0.05, seed=203,
+      cov_norm="spectral"),
+    W("spec_bf16_d64_blk64", 2, 1, 777, 64, 64, 0.3, "bf16", "pb1", None, 0.02, seed=204, cov_norm="spectral"),
+    W("spec_edge_single_block", 1, 2, 40, 128, 64, 0.5, "bf16", "hyd", None, 0.1, seed=205,
+      cov_norm="spectral"),
+    W("spec_edge_last_block_one_token", 1, 2, 65, 128, 64, 0.5, "bf16", "hyd", -1, 0.1, seed=206,
+      cov_norm="spectral"),
+]
+
+
+@pytest.mark.parametrize("w", SPECTRAL, ids=lambda w: w.name)
+def test_spectral_covariance_routing(w):
+    check_workload(w)
+
+
+def test_flux_config_spectral_norm():
+    """The FLUX configuration (covariance routing at weight 0.1, sink 0) with
+    the spectral norm: statistics, every selection row (tie rule) and every
+    output against the oracle."""
+    check_workload(synth.FLUX.replace(name="flux_bf16_spectral", cov_norm="spectral"))
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("rel_gap", [0.0, 2.0 ** -7])
+def test_spectral_norm_repeated_top_singular_value(D, rel_gap):
+    """Two blocks built so that H_0 − H̄ = 16 (e_0 u_0ᵀ + e_1 u_1ᵀ) with
+    u_0 = 2 e_2 and u_1 = 2 (1 + gap) e_3, and H_1 − H̄ its negative: the two
+    largest singular values are 32 and 32 (1 + gap), equal or 2^-7 apart, where
+    a power iteration would stall. Every input is a small integer or a
+    power-of-two fraction, exact in bf16, so the spectral norm must come out as
+    32 (1 + gap) to fp64 accuracy."""
+    L = 128
+    k = torch.zeros(1, 1, L, D)
+    v = torch.zeros(1, 1, L, D)
+    for t in range(64):  # block 0: k_t = ±e_{t%2}, v_t = ±u_{t%2}, signs alternating in pairs
+        s = 1.0 if (t // 2) % 2 == 0 else -1.0
+        k[0, 0, t, t % 2] = s
+        v[0, 0, t, 2 + t % 2] = s * 2.0 * (1.0 + (rel_gap if t % 2 else 0.0))
+    k[0, 0, 64:, 5] = 3.0  # block 1: constant keys, so H_1 = 0
+    v[0, 0, 64:, 7] = torch.arange(64, dtype=torch.float32) - 20.0
+    q = torch.ones(1, 1, L, D)
+    dev = torch.device("cuda:0")
+    qd, kd, vd = (x.to(torch.bfloat16).to(dev) for x in (q, k, v))
+    st = bsa.block_stats(qd, kd, vd, 64, want_mnorm=True, cov_norm="spectral")
+    st_f = bsa.block_stats(qd, kd, vd, 64, want_mnorm=True, cov_norm="fro")
+    torch.cuda.synchronize()
+    want = 32.0 * (1.0 + rel_gap)
+    got = st.mnorm.cpu().numpy()[0, 0]
+    np.testing.assert_allclose(got, [want, want], rtol=1e-13, atol=0)
+    fro = math.sqrt(32.0 ** 2 + want ** 2)
+    np.testing.assert_allclose(st_f.mnorm.cpu().numpy()[0, 0], [fro, fro], rtol=1e-6)
 
 
 def test_tiny_config_full():
