@@ -234,6 +234,74 @@ def head_forward(q, k, v, *, block: int, topk: int, scale: float, variant: str =
     return o, idx
 
 
+def head_backward(q, k, v, do, *, block: int, idx: np.ndarray, scale: float):
+    """Gradients of the zeroth-order-only forward pass (README, "Kernel
+    variants": the ``_0th`` variant is the one that supports training) with
+    respect to q, k and v, for one (batch, head), the selection ``idx`` held
+    fixed. q, k, v, do: [L, D] float64; returns (dq, dk, dv).
+
+    The forward pass (gist, "Core Algorithm", N_t equation without the
+    first-order term) is o_t = N_t / D_t with
+      N_t = Σ_{S_i} Σ_n e^{ℓ_tn} v_n + Σ_{U_i} α_tj ΣV_j,
+      D_t = Σ_{S_i} Σ_n e^{ℓ_tn}   + Σ_{U_i} n_j α_tj,
+    ℓ_tn = s q_t·k_n, α_tj = e^{s q_t·k̄_j}. Writing p_tn = e^{ℓ_tn} / D_t and
+    a_tj = α_tj / D_t, the chain rule gives, with Δ_t = dO_t·o_t:
+      ∂L/∂ℓ_tn = p_tn (dO_t·v_n − Δ_t),
+      ∂L/∂c_tj = a_tj (dO_t·ΣV_j − n_j Δ_t)        (c_tj = s q_t·k̄_j),
+      dq_t    = s [Σ_{S_i} Σ_n ∂L/∂ℓ_tn k_n + Σ_{U_i} ∂L/∂c_tj k̄_j],
+      dk_n   += s Σ_t ∂L/∂ℓ_tn q_t,  dv_n += Σ_t p_tn dO_t   (rows t whose block selects n's),
+      dk̄_j   += s Σ_t ∂L/∂c_tj q_t,  dΣV_j += Σ_t a_tj dO_t (rows t whose block leaves j out),
+    and k̄_j = (1/n_j) Σ_{n∈j} k_n, ΣV_j = Σ_{n∈j} v_n pass dk̄_j / n_j and
+    dΣV_j on to every token of block j."""
+    L, D = q.shape
+    n = num_blocks(L, block)
+    sizes = block_sizes(L, block).astype(np.float64)
+    st = block_stats(q, k, v, block)
+    kbar, vsum = st["kbar"], st["vsum"]
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dkbar = np.zeros((n, D))
+    dvsum = np.zeros((n, D))
+    span = lambda j: slice(j * block, min(L, (j + 1) * block))
+    for i in range(n):
+        rows = span(i)
+        Qi, dOi = q[rows], do[rows]
+        sel = np.asarray(idx[i])
+        mask = np.ones(n, dtype=bool)
+        mask[sel] = False
+        uns = np.nonzero(mask)[0]
+        Ksel = np.concatenate([k[span(j)] for j in sel])
+        Vsel = np.concatenate([v[span(j)] for j in sel])
+        ell = scale * (Qi @ Ksel.T)
+        c = scale * (Qi @ kbar[uns].T)
+        m = ell.max(axis=1)
+        if uns.size:
+            m = np.maximum(m, c.max(axis=1))
+        P = np.exp(ell - m[:, None])
+        A = np.exp(c - m[:, None])
+        Dt = P.sum(axis=1) + A @ sizes[uns]
+        o = (P @ Vsel + A @ vsum[uns]) / Dt[:, None]
+        p, a = P / Dt[:, None], A / Dt[:, None]
+        delta = (dOi * o).sum(axis=1)
+        dl = p * (dOi @ Vsel.T - delta[:, None])
+        dc = a * (dOi @ vsum[uns].T - sizes[uns][None, :] * delta[:, None])
+        dq[rows] = scale * (dl @ Ksel + dc @ kbar[uns])
+        dK, dV = scale * (dl.T @ Qi), p.T @ dOi
+        off = 0
+        for j in sel:
+            nj = int(sizes[j])
+            dk[span(j)] += dK[off:off + nj]
+            dv[span(j)] += dV[off:off + nj]
+            off += nj
+        dkbar[uns] += scale * (dc.T @ Qi)
+        dvsum[uns] += a.T @ dOi
+    for j in range(n):
+        dk[span(j)] += dkbar[j] / sizes[j]
+        dv[span(j)] += dvsum[j]
+    return dq, dk, dv
+
+
 def effective_flops(L: int, D: int, block: int, idx: np.ndarray, first_order: bool,
                     per_block: bool = False) -> float:
     """Credited FLOPs of the fused pass for one (batch, head): 4·D per exact
