@@ -197,6 +197,9 @@ def main():
     ap.add_argument("--pb1-reps", type=int, default=2,
                     help="calls of the per-block first-order variant timed on the same selection")
     ap.add_argument("--no-pb1", action="store_true")
+    ap.add_argument("--bwd-reps", type=int, default=2,
+                    help="calls of the zeroth-order variant's backward pass timed on the step's selection")
+    ap.add_argument("--no-bwd", action="store_true")
     ap.add_argument("--banded-reps", type=int, default=3,
                     help="calls of the fused pass timed on a local (banded) selection of the same size")
     ap.add_argument("--no-banded", action="store_true")
@@ -331,6 +334,33 @@ def main():
         print(f"[bench] pb1 {pms:.2f} ms, {pb1['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
         del op
 
+    bwd = None
+    if not args.no_bwd:
+        # backward of the zeroth-order variant on the step's statistics and
+        # selection, with a seeded upstream gradient of the output's shape
+        gen = torch.Generator(device=dev).manual_seed(w.seed)
+        dout = torch.randn(qd.shape, generator=gen, device=dev, dtype=torch.float32).to(qd.dtype)
+        o0 = bsa.attn_fwd(qd, st, idx, s, "0th")
+        bws = torch.empty(bsa.load_library().pisa_bwd_workspace_bytes(bsa.ctypes.byref(shape)),
+                          dtype=torch.uint8, device=dev)
+        bsa.attn_bwd(qd, kd, vd, st, idx, s, o0, dout, ws=bws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.bwd_reps):
+            bsa.attn_bwd(qd, kd, vd, st, idx, s, o0, dout, ws=bws)
+        e1.record()
+        torch.cuda.synchronize()
+        bwd_ms = e0.elapsed_time(e1) / args.bwd_reps
+        f0 = flops_from_idx(idx.cpu().numpy(), w.L, w.D, w.block, False)
+        bflops = 2.5 * (f0["exact"] + f0["tail"])  # five products per (query, key or centroid) pair
+        bwd = {"kernel": "pisa_attn_bwd (zeroth-order variant)", "ms": bwd_ms, "flops": bflops,
+               "tflops": bflops / (bwd_ms * 1e-3) / 1e12,
+               "mfma_frac": bflops / (bwd_ms * 1e-3) / 1e12 / peak,
+               "ms_vs_fwd_fused": bwd_ms / ms["attn_fwd"]}
+        print(f"[bench] backward (0th) {bwd_ms:.2f} ms, {bwd['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
+        del dout, o0, bws
+
     banded = None
     if not args.no_banded:
         # the same fused pass on a local selection: query block i takes the topk
@@ -389,6 +419,7 @@ def main():
         "dense": dense,
         "pb1": pb1,
         "banded": banded,
+        "bwd": bwd,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

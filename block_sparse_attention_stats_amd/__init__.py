@@ -33,7 +33,8 @@ PISA_F32, PISA_BF16 = 0, 1
 PISA_SINK_NONE = -(2 ** 31)
 EXPORTS = ("pisa_workspace_bytes", "pisa_block_stats", "pisa_select", "pisa_attn_fwd",
            "dense_workspace_bytes", "dense_attn_fwd", "pisa_status_string", "pisa_last_hip_error",
-           "pisa_block_stats_seg", "pisa_attn_fwd_seg", "dense_attn_fwd_seg", "pisa_attn_fwd_noalloc")
+           "pisa_block_stats_seg", "pisa_attn_fwd_seg", "dense_attn_fwd_seg", "pisa_attn_fwd_noalloc",
+           "pisa_bwd_workspace_bytes", "pisa_attn_bwd")
 
 
 class PisaError(RuntimeError):
@@ -100,6 +101,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pisa_attn_fwd_seg": (I32, [SP, P, STP, I32, P, I32, D64, P, SG, P]),
         "dense_attn_fwd_seg": (I32, [SP, P, P, P, SG, D64, P, P, SZ, P]),
         "pisa_attn_fwd_noalloc": (I32, [SP, P, P, P, I32, P, I32, D64, P, P]),
+        "pisa_bwd_workspace_bytes": (SZ, [SP]),
+        "pisa_attn_bwd": (I32, [SP, P, P, P, STP, P, I32, D64, P, P, P, P, P, P, SZ, P]),
         "pisa_status_string": (ctypes.c_char_p, [I32]),
         "pisa_last_hip_error": (ctypes.c_char_p, []),
     }
@@ -390,6 +393,59 @@ def attn_fwd_noalloc(q, k, v, idx: torch.Tensor, scale: float, first_order=True,
     return o
 
 
+def attn_bwd(q, k, v, st: Stats, idx: torch.Tensor, scale: float, o, dout, ws: torch.Tensor | None = None):
+    """Backward pass of the zeroth-order-only variant via pisa_attn_bwd: the
+    gradients (dq, dk, dv) of Σ o∘dout, with the selection idx held fixed. q,
+    k, v, st and idx are those of the forward call and o its output."""
+    _check_qkv(q, k, v)
+    shape = st.shape
+    st.check()
+    for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
+        _check_io(t, shape, name)
+    topk = _check_idx(idx, shape)
+    lib = load_library()
+    nbytes = lib.pisa_bwd_workspace_bytes(ctypes.byref(shape))
+    if nbytes == 0:
+        raise PisaError(PISA_EINVAL, "pisa_bwd_workspace_bytes")
+    if ws is not None and (ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous()):
+        raise ValueError("ws must be a contiguous 1-D uint8 tensor")
+    _on_gpu(q, k, v, o, dout, idx, *st.tensors(), *(() if ws is None else (ws,)))
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    sst = st.struct()
+    _check(lib.pisa_attn_bwd(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(sst),
+                             idx.data_ptr(), topk, float(scale), o.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                             dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
+           "pisa_attn_bwd")
+    return dq, dk, dv
+
+
+class _Pisa0th(torch.autograd.Function):
+    """The zeroth-order-only variant with a backward pass: forward through
+    pisa_block_stats, pisa_select and pisa_attn_fwd, backward through
+    pisa_attn_bwd (the selection held fixed)."""
+
+    @staticmethod
+    def forward(ctx, q, k, v, density, block_size, sink_idx, cov_weight, scale, layout, cov_norm):
+        shape = make_shape(q, block_size, layout)
+        s = 1.0 / math.sqrt(shape.D) if scale is None else float(scale)
+        topk = topk_from_density(density, num_blocks(shape.L, block_size))
+        st = block_stats(q, k, v, block_size, want_mnorm=cov_weight > 0, layout=layout, cov_norm=cov_norm)
+        idx = select(st, topk, s, cov_weight, sink_idx)
+        o = attn_fwd(q, st, idx, s, False)
+        ctx.save_for_backward(q, k, v, o, idx)
+        ctx.st, ctx.scale = st, s
+        ctx.mark_non_differentiable(idx)
+        return o, idx
+
+    @staticmethod
+    def backward(ctx, do, _didx):
+        q, k, v, o, idx = ctx.saved_tensors
+        dq, dk, dv = attn_bwd(q, k, v, ctx.st, idx, ctx.scale, o, do.contiguous())
+        return dq, dk, dv, None, None, None, None, None, None, None
+
+
 def dense(q, k, v, scale: float | None = None, out: torch.Tensor | None = None,
           ws: torch.Tensor | None = None, layout: str = "BHLD") -> torch.Tensor:
     """Same-device dense attention baseline, softmax(scale·QKᵀ)V."""
@@ -435,7 +491,14 @@ def piecewise_sparse_attention_hyd(q, k, v, density: float = 0.15, block_size: i
 def piecewise_sparse_attention_0th(q, k, v, density: float = 0.15, block_size: int = 64,
                                    sink_idx=None, cov_weight: float = 0.0, scale=None,
                                    return_idx: bool = False, layout: str = "BHLD", cov_norm: str = "fro"):
-    """PISA forward, zeroth-order-only variant (no global first-order term)."""
+    """PISA forward, zeroth-order-only variant (no global first-order term).
+    When q, k or v requires a gradient (and autograd is on), the call records
+    a backward pass through pisa_attn_bwd, as the README's training example
+    uses it (``out_0th.backward(...)``)."""
+    if torch.is_grad_enabled() and any(t.requires_grad for t in (q, k, v)):
+        _check_qkv(q, k, v)
+        o, idx = _Pisa0th.apply(q, k, v, density, block_size, sink_idx, cov_weight, scale, layout, cov_norm)
+        return (o, idx) if return_idx else o
     return piecewise_sparse_attention_hyd(q, k, v, density, block_size, sink_idx, cov_weight, scale,
                                           first_order=False, return_idx=return_idx, layout=layout,
                                           cov_norm=cov_norm)

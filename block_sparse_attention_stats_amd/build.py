@@ -15,7 +15,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpisa.so")
-SOURCES = ["k_stats.hip", "k_mnorm.hip", "k_select.hip", "k_fwd.hip", "pisa_abi.hip"]
+SOURCES = ["k_stats.hip", "k_mnorm.hip", "k_select.hip", "k_fwd.hip", "k_bwd.hip", "pisa_abi.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -381,6 +381,83 @@ PISA_API pisa_status_t pisa_attn_fwd_noalloc(const pisa_shape_t* shape, const vo
   return hip_status(pisa::launch_fwd(shape->dtype, shape->D, a, s));
 }
 
+namespace {
+
+pisa::BwdLayout bwd_layout(const pisa_shape_t* s, const pisa::WsLayout& w) {
+  pisa::BwdLayout b;
+  const int W = (w.n + 31) / 32;
+  size_t off = 0;
+  b.selmap = off;
+  off = align256(off + (size_t)w.bh * w.n * W * sizeof(uint32_t));
+  b.lse = off;
+  off = align256(off + (size_t)w.bh * w.n * s->block * sizeof(float));
+  b.delta = off;
+  off = align256(off + (size_t)w.bh * w.n * s->block * sizeof(float));
+  b.dkbar = off;
+  off = align256(off + (size_t)w.bh * w.n * s->D * sizeof(float));
+  b.dvsum = off;
+  off = align256(off + (size_t)w.bh * w.n * s->D * sizeof(float));
+  b.total = off;
+  return b;
+}
+
+}  // namespace
+
+PISA_API size_t pisa_bwd_workspace_bytes(const pisa_shape_t* shape) {
+  pisa::WsLayout w;
+  return check_shape(shape, &w) == PISA_OK ? bwd_layout(shape, w).total : 0;
+}
+
+PISA_API pisa_status_t pisa_attn_bwd(const pisa_shape_t* shape, const void* q, const void* k,
+                                     const void* v, const pisa_stats_t* st, const int32_t* idx,
+                                     int32_t topk, double scale, const void* o, const void* dout,
+                                     void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  pisa::WsLayout w;
+  pisa_status_t rc = check_shape(shape, &w);
+  if (rc != PISA_OK) return rc;
+  const void* in[] = {q, k, v, o, dout, dq, dk, dv};
+  for (const void* p : in)
+    if (!tensor_ok(p)) return PISA_EINVAL;
+  if (!(scale > 0.0) || !isfinite(scale)) return PISA_EINVAL;
+  if (topk < 1 || topk > w.n) return PISA_EINVAL;
+  if (idx == nullptr || !aligned(idx, 4)) return PISA_EINVAL;
+  if (st == nullptr || st->kbar == nullptr || st->vsum == nullptr || !aligned(st->kbar, 8) ||
+      !aligned(st->vsum, 8))
+    return PISA_EINVAL;
+  const pisa::BwdLayout bl = bwd_layout(shape, w);
+  if (ws == nullptr || !aligned(ws, 256) || ws_bytes < bl.total) return PISA_EINVAL;
+  uint8_t* base = (uint8_t*)ws;
+  pisa::BwdArgs a;
+  a.q = (const uint8_t*)q;
+  a.k = (const uint8_t*)k;
+  a.v = (const uint8_t*)v;
+  a.o = (const uint8_t*)o;
+  a.dout = (const uint8_t*)dout;
+  a.dq = (uint8_t*)dq;
+  a.dk = (uint8_t*)dk;
+  a.dv = (uint8_t*)dv;
+  io_strides(shape, shape->L, &a.stride_b, &a.stride_h, &a.stride_l);
+  a.H = shape->H;
+  a.kbar = st->kbar;
+  a.vsum = st->vsum;
+  a.idx = idx;
+  a.selmap = (uint32_t*)(base + bl.selmap);
+  a.lse = (float*)(base + bl.lse);
+  a.delta = (float*)(base + bl.delta);
+  a.dkbar = (float*)(base + bl.dkbar);
+  a.dvsum = (float*)(base + bl.dvsum);
+  a.L = shape->L;
+  a.n = w.n;
+  a.blk = shape->block;
+  a.n_last = shape->L - (w.n - 1) * shape->block;
+  a.nct = w.nct;
+  a.topk = topk;
+  a.W = (w.n + 31) / 32;
+  a.scale = (float)scale;
+  return hip_status(pisa::launch_bwd(shape->dtype, shape->D, a, w.bh, (hipStream_t)stream));
+}
+
 PISA_API pisa_status_t dense_attn_fwd_seg(const pisa_shape_t* shape, const void* q, const void* k,
                                           const void* v, const pisa_segments_t* seg, double scale,
                                           void* o, void* ws, size_t ws_bytes, void* stream) {

@@ -77,6 +77,26 @@ struct FwdArgs {
   int H, L0;
 };
 
+// Backward pass of the zeroth-order variant.
+struct BwdArgs {
+  const uint8_t *q, *k, *v, *o, *dout;  // [B,H,L,D] or [B,L,H,D], I/O dtype
+  uint8_t *dq, *dk, *dv;
+  size_t stride_b, stride_h, stride_l;  // byte strides, as in StatsArgs
+  int H;
+  const double *kbar, *vsum;  // block statistics of the forward pass: [BH][n][D] fp64
+  const int32_t* idx;         // [BH][n][topk]
+  uint32_t* selmap;           // [BH][n][W]: bit j of row i set when query block i selects j
+  float *lse, *delta;         // [BH][n*blk]: log2 of each row's denominator, dO·o
+  float *dkbar, *dvsum;       // [BH][n][D]: gradients of k̄_j and ΣV_j
+  int L, n, blk, n_last, nct, topk, W;
+  float scale;
+};
+
+// Byte offsets of the backward workspace regions (all 256-aligned).
+struct BwdLayout {
+  size_t selmap, lse, delta, dkbar, dvsum, total;
+};
+
 enum StatsMode { kStatsFull = 0, kStatsMnorm = 1, kStatsPackOnly = 2 };
 
 // Each returns hipGetLastError() after enqueueing.
@@ -89,6 +109,10 @@ hipError_t launch_scores(int D, const ScoreArgs& a, long bh, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, long rows, hipStream_t s);
 // Fast pass, then the careful pass over the query tiles the fast pass queued.
 hipError_t launch_fwd(int dtype, int D, const FwdArgs& a, hipStream_t s);
+
+// Backward of the zeroth-order variant: selection bitmap, dq (with the row
+// statistics), centroid gradients, then dk and dv.
+hipError_t launch_bwd(int dtype, int D, const BwdArgs& a, long bh, hipStream_t s);
 
 constexpr int kMaxBlocks = 8192;  // routing keeps one score row per workgroup in LDS
 

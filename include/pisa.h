@@ -174,6 +174,31 @@ pisa_status_t pisa_attn_fwd(const pisa_shape_t *shape, const void *q, const pisa
                             int32_t first_order, const int32_t *idx, int32_t topk, double scale,
                             void *o, void *stream);
 
+/* Backward pass of the zeroth-order-only variant (first_order = 0), the form
+ * the README's "Kernel variants" names as the one that supports training.
+ * With the selection idx held fixed, the gradients of L = Σ o∘dout follow from
+ * the N_t / D_t of pisa_attn_fwd by the chain rule; the block centroid k̄_j
+ * and the value sum ΣV_j of an unselected block pass their gradients on to
+ * every token of block j (dk_n gets dk̄_j / n_j, dv_n gets dΣV_j).
+ *   q, k, v   the forward's inputs (one tensor each; shape->layout as there)
+ *   st        the forward's statistics: st->kbar and st->vsum are read (the
+ *             workspace copies are not)
+ *   idx, topk the forward's selection, as for pisa_attn_fwd
+ *   o         the forward's output (o_t enters through Δ_t = dout_t·o_t)
+ *   dout      the gradient of the loss with respect to o
+ *   dq, dk, dv receive the gradients, shaped and typed like q, k, v
+ *   ws        at least pisa_bwd_workspace_bytes(shape) bytes, 256-aligned:
+ *             the selection as a bitmap, each row's log-sum of weights and
+ *             Δ_t, and the fp32 gradients of k̄ and ΣV
+ * Products run on the matrix cores with fp32 accumulation; the weights and
+ * their gradients are rounded to the I/O dtype as operands. Deterministic.
+ * Errors as for pisa_attn_fwd. */
+size_t pisa_bwd_workspace_bytes(const pisa_shape_t *shape);
+pisa_status_t pisa_attn_bwd(const pisa_shape_t *shape, const void *q, const void *k, const void *v,
+                            const pisa_stats_t *st, const int32_t *idx, int32_t topk, double scale,
+                            const void *o, const void *dout, void *dq, void *dk, void *dv, void *ws,
+                            size_t ws_bytes, void *stream);
+
 /* pisa_block_stats followed by pisa_attn_fwd in one call that allocates
  * nothing and takes no workspace, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that

@@ -132,6 +132,20 @@ def make_qkv(w: Workload, heads: list[tuple[int, int]] | None = None):
     return q, k, v
 
 
+def grad_out(w: Workload):
+    """A seeded upstream gradient dO ~ N(0, 1), shaped [B, H, L, D] like the
+    workload's q and rounded to its I/O dtype (CPU torch tensor); drawn per
+    (b, h) from ``numpy.random.default_rng([seed, b, h, 1])``."""
+    import torch
+    dt = torch_dtype(w.dtype)
+    out = torch.empty((w.B, w.H, w.L, w.D), dtype=dt)
+    for b in range(w.B):
+        for h in range(w.H):
+            rng = np.random.default_rng([w.seed, b, h, 1])
+            out[b, h] = torch.from_numpy(rng.standard_normal((w.L, w.D), dtype=np.float32)).to(dt)
+    return out
+
+
 def integer_qkv(B: int, H: int, L: int, D: int, seed: int, key_period: int | None = None,
                 amp: int = 4):
     """q, k, v as CPU bf16 tensors [B, H, L, D] of small integers in [-amp, amp],

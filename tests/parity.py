@@ -200,3 +200,69 @@ def check_workload(w: synth.Workload, heads=None, qblock_sample: int | None = No
     log(f"[{w.name}] ok in {time.time() - t0:.1f}s; idx rows differing within ties: {res['differ_rows']}")
     res["stats"] = st
     return res
+
+
+# Gradients (backward of the zeroth-order variant), relative to the largest
+# reference entry of each tensor: the kernels round the weights p̃ and their
+# gradients dS to the I/O dtype as matrix-core operands (relative 2^-9 for
+# bf16) and use the forward's rounded output for Δ_t = dO_t·o_t, so each
+# gradient entry is off by a few 2^-9 of the sum of its terms' magnitudes.
+# On top of that an absolute floor: dS_tx = p̃_tx (dO_t·V'_x − w_x Δ_t) takes
+# the difference of two D-term fp32 dot products, each off by up to
+# γ_D |dO_t|·|v|, which s·|k| (or s·|q|) carries into dq (dk); where the two
+# cancel (a single key: o = v and dq = 0) that floor is all that is left.
+GRAD_TOL = {"bf16": dict(max_rel=2e-2, rms_rel=1e-2), "f32": dict(max_rel=1e-4, rms_rel=1e-4)}
+
+
+def compare_grad(gpu: np.ndarray, ref: np.ndarray, dtype: str, what: str, floor: float = 0.0):
+    err = np.abs(gpu.astype(np.float64) - ref)
+    scale = float(np.abs(ref).max())
+    rms_ref = float(np.sqrt((ref ** 2).mean()))
+    tol = GRAD_TOL[dtype]
+    mx, rms = float(err.max()), float(np.sqrt((err ** 2).mean()))
+    bar_mx, bar_rms = tol["max_rel"] * scale + floor, tol["rms_rel"] * rms_ref + floor
+    log(f"    {what}: max-abs {mx:.3e} (bar {bar_mx:.3e} = {tol['max_rel']:.0e} x max|ref| + floor {floor:.1e}), "
+        f"rms {rms:.3e} (bar {bar_rms:.3e})")
+    assert np.isfinite(gpu).all(), f"{what}: non-finite gradient"
+    assert mx <= bar_mx, f"{what}: max-abs {mx} > {bar_mx}"
+    assert rms <= bar_rms, f"{what}: rms {rms} > {bar_rms}"
+
+
+def grad_floor(q, k, v, do, scale: float, D: int) -> float:
+    """The absolute floor above, for one head's fp64 inputs."""
+    nrm = lambda x: float(np.sqrt((x * x).sum(axis=1)).max())
+    return 2.0 * gamma(D) * scale * nrm(do) * nrm(v) * max(nrm(k), nrm(q)) + 1e-30
+
+
+def check_backward(w: synth.Workload, heads=None):
+    """The backward pass on the GPU (all heads, the oracle's selection, the
+    GPU's own forward output) against the oracle's gradients on `heads`."""
+    t0 = time.time()
+    log(f"[{w.name}] backward B={w.B} H={w.H} L={w.L} D={w.D} blk={w.block} d={w.density} "
+        f"sink={w.sink_idx} {w.dtype}")
+    q, k, v = synth.make_qkv(w)
+    do = synth.grad_out(w)
+    dev = torch.device("cuda:0")
+    qd, kd, vd, dod = (x.to(dev) for x in (q, k, v, do))
+    n = w.n_blocks
+    topk = bsa.topk_from_density(w.density, n)
+    heads = heads if heads is not None else [(b, h) for b in range(w.B) for h in range(w.H)]
+    idx = np.zeros((w.B, w.H, n, topk), dtype=np.int64)
+    for (b, h) in heads:
+        qh, kh, vh = (synth.as_f64(x[b, h]) for x in (q, k, v))
+        _, idx[b, h] = oracle.head_forward(qh, kh, vh, block=w.block, topk=topk, scale=w.scale, variant="0th",
+                                           sink_idx=w.sink_idx, cov_weight=w.cov_weight, cov_ord=w.cov_norm)
+    idx_d = torch.from_numpy(idx.astype(np.int32)).to(dev)
+    st = bsa.block_stats(qd, kd, vd, w.block)
+    o = bsa.attn_fwd(qd, st, idx_d, w.scale, "0th")
+    dq, dk, dv = bsa.attn_bwd(qd, kd, vd, st, idx_d, w.scale, o, dod)
+    torch.cuda.synchronize()
+    g = [x.float().cpu().numpy() for x in (dq, dk, dv)]
+    for (b, h) in heads:
+        qh, kh, vh, doh = (synth.as_f64(x[b, h]) for x in (q, k, v, do))
+        ref = oracle.head_backward(qh, kh, vh, doh, block=w.block, idx=idx[b, h], scale=w.scale)
+        fl = grad_floor(qh, kh, vh, doh, w.scale, w.D)
+        for name, gg, rr in zip(("dq", "dk", "dv"), g, ref):
+            compare_grad(gg[b, h], rr, w.dtype, f"head ({b},{h}) {name}", fl)
+    log(f"[{w.name}] backward ok in {time.time() - t0:.1f}s")
+    return dict(st=st, idx=idx_d, o=o, grads=(dq, dk, dv), inputs=(qd, kd, vd, dod))
