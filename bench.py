@@ -79,17 +79,39 @@ def flops_from_idx(idx: np.ndarray, L: int, D: int, block: int, first_order: boo
     return dict(exact=exact, tail=tail, corr=corr, total=exact + tail + corr)
 
 
-def stats_bytes(B, H, L, D, block, esz) -> float:
-    """Algorithmic bytes of the statistics pass: q, k, v read once; operand
-    copies of K and V (2·L·D·esz), block statistics (3·n·D fp64), k̄ and ΣV
-    tiles, per-run partial sums and H̄ written."""
+def stats_bytes(B, H, L, D, block, esz) -> dict:
+    """Bytes of the statistics pass per call. ``algorithmic``: q, k, v read once;
+    q̄, k̄, ΣV (fp64), the k̄ / ΣV centroid tiles and H̄ᵀ in the I/O dtype, H̄
+    (fp64) and the largest key norms written. ``copies``: the operand-ordered
+    copies of K and V for the fused pass (written). ``partials``: the per-run
+    partial sums of H_j (written, then read once by the reduction to H̄)."""
     n = -(-L // block)
     bh = B * H
-    read = 3.0 * L * D * esz
-    write = 2.0 * n * block * D * esz + 3.0 * n * D * 8 + 2.0 * (-(-n // 64)) * 64 * D * esz
+    nct = -(-n // 64)
     cb = min(1024 // block, max(1, bh * n // 512))  # blocks per statistics run
-    write += (-(-n // cb)) * D * D * 4
-    return bh * (read + write)
+    nch = -(-n // cb)
+    alg = 3.0 * L * D * esz + 3.0 * n * D * 8 + 2.0 * nct * 64 * D * esz + D * D * (8 + esz) + nch * 4
+    copies = 2.0 * n * (block // 64) * 64 * D * esz
+    partials = 2.0 * nch * D * D * 4
+    return {"algorithmic": bh * alg, "copies": bh * copies, "partials": bh * partials}
+
+
+def copy_bandwidth(dev, nbytes: int = 2 << 30) -> float:
+    """GB/s of one plain device-to-device copy (read + write counted)."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2.0 * nbytes * 3 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    return gbs
 
 
 def cpu_baseline(w, budget_s: float = 15.0) -> dict:
@@ -289,6 +311,7 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     esz = 2 if w.dtype == "bf16" else 4
     sbytes = stats_bytes(w.B, w.H, w.L, w.D, w.block, esz)
+    copy_gbs = copy_bandwidth(dev)
     print(f"[bench] step {ms_step:.3f} ms: stats {ms['block_stats']:.3f} select {ms['select']:.3f} "
           f"fused {ms['attn_fwd']:.3f}; fused {fused_tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
@@ -411,8 +434,13 @@ def main():
         "flops": f,
         "fused_tflops": fused_tflops,
         "exact_phase_mfma_frac": f["exact"] / (ms["attn_fwd"] * 1e-3) / 1e12 / peak,
-        "stats_gbs": sbytes / (ms["block_stats"] * 1e-3) / 1e9,
-        "stats_hbm_frac": sbytes / (ms["block_stats"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        # the statistics pass on its algorithmic bytes; the K/V operand copies and
+        # the partial sums of H_j it also writes are given apart
+        "stats_gbs": sbytes["algorithmic"] / (ms["block_stats"] * 1e-3) / 1e9,
+        "stats_hbm_frac": sbytes["algorithmic"] / (ms["block_stats"] * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "stats_bytes": sbytes,
+        "stats_all_bytes_gbs": sum(sbytes.values()) / (ms["block_stats"] * 1e-3) / 1e9,
+        "hbm_copy_gbs": copy_gbs,  # measured device copy, next to the 8 TB/s spec peak
         "roofline": {"kernel": "k_pisa_fwd", "bound": "mfma", "achieved": fused_tflops, "peak": peak,
                      "unit": "TFLOP/s", "frac": fused_tflops / peak,
                      "traffic": fused_traffic(w.name), "traffic_unit": "bytes per launch"},
