@@ -77,36 +77,41 @@ __device__ __forceinline__ size_t row_off(const BwdArgs& a, long bh, int row) {
   return (size_t)(bh / a.H) * a.stride_b + (size_t)(bh % a.H) * a.stride_h + (size_t)row * a.stride_l;
 }
 
-// Rows r0 .. r0+63 of a tensor into an LDS tile (zero past L).
+// A run of rows: row g at base + g * pitch, rows from `limit` on read as zero.
+struct Rows {
+  const uint8_t* base;
+  size_t pitch;
+  int limit;
+};
+
+__device__ __forceinline__ Rows tensor_rows(const BwdArgs& a, const uint8_t* t, long bh) {
+  return Rows{t + row_off(a, bh, 0), a.stride_l, a.L};
+}
+
 template <typename T, int D>
-__device__ __forceinline__ void stage_rows(uint8_t* tile, const uint8_t* src, const BwdArgs& a, long bh,
-                                           int r0) {
+__device__ __forceinline__ Rows centroid_rows(const BwdArgs& a, const uint8_t* t, long bh) {
+  return Rows{t + (size_t)bh * a.nct * 64 * D * sizeof(T), (size_t)D * sizeof(T), a.nct * 64};
+}
+
+// Issues the loads of rows r0 .. r0+63 into registers (one tile's share of this thread).
+template <typename T, int D>
+__device__ __forceinline__ void load_rows(const Rows& s, int r0, uint4 (&pre)[BT<T, D>::PER]) {
   using B = BT<T, D>;
 #pragma unroll
   for (int i = 0; i < B::PER; ++i) {
     const int x = threadIdx.x + 256 * i, row = x / B::CPR, cc = x % B::CPR;
     const int g = r0 + row;
-    const uint4 val = g < a.L ? *(const uint4*)(src + row_off(a, bh, g) + cc * 16) : make_uint4(0, 0, 0, 0);
-    *(uint4*)(tile + row * B::RP + cc * 16) = val;
+    pre[i] = g < s.limit ? *(const uint4*)(s.base + (size_t)g * s.pitch + cc * 16) : make_uint4(0, 0, 0, 0);
   }
 }
 
-// Rows 64 ct .. 64 ct + 63 of an fp64 [n][D] statistic of head bh, rounded to T
-// (zero past n).
 template <typename T, int D>
-__device__ __forceinline__ void stage_stat(uint8_t* tile, const double* src, const BwdArgs& a, long bh,
-                                           int ct) {
+__device__ __forceinline__ void store_rows(uint8_t* tile, const uint4 (&pre)[BT<T, D>::PER]) {
   using B = BT<T, D>;
-  using O = Op<T>;
 #pragma unroll
   for (int i = 0; i < B::PER; ++i) {
     const int x = threadIdx.x + 256 * i, row = x / B::CPR, cc = x % B::CPR;
-    const int j = 64 * ct + row;
-    T vals[B::KW];
-#pragma unroll
-    for (int e = 0; e < B::KW; ++e)
-      vals[e] = O::from_f32(j < a.n ? (float)src[((size_t)bh * a.n + j) * D + cc * B::KW + e] : 0.0f);
-    *(uint4*)(tile + row * B::RP + cc * 16) = __builtin_bit_cast(uint4, vals);
+    *(uint4*)(tile + row * B::RP + cc * 16) = pre[i];
   }
 }
 
@@ -144,10 +149,13 @@ __device__ __forceinline__ void merge_halves(f32x16 (&acc)[DT], float* xf, int s
 // ---------------------------------------------------------------------------
 // dq, with the rows' log2 D_t and Δ_t. Wavefront w = (xh, th): Sᵀ quadrant of
 // key half xh x row half th; its dq partial covers rows th and sums keys xh.
+// Both sweeps run over the same key tiles (the selected blocks' 64-key
+// sub-tiles, then the centroid tiles); the rows of tile u+1 load into
+// registers while tile u is computed.
 template <typename T, int D, int SPB>
 __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
   using B = BT<T, D>;
-  constexpr int KW = B::KW, NC = B::NC, DT = B::DT, CPK = B::CPK;
+  constexpr int KW = B::KW, NC = B::NC, DT = B::DT, CPK = B::CPK, PER = B::PER;
   __shared__ __align__(16) uint8_t qt[B::TILE], ot[B::TILE];
   __shared__ __align__(16) uint8_t kv[2 * B::TILE];  // key and value tiles; partial sums at the end
   __shared__ float lse_s[64], dl_s[64], wx_s[64];
@@ -167,8 +175,43 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
   if (r0 >= a.L) return;
   const float cs = a.scale * kLog2e;
 
-  stage_rows<T, D>(qt, a.q, a, bh, r0);
-  stage_rows<T, D>(ot, a.dout, a, bh, r0);
+  const Rows krows = tensor_rows(a, a.k, bh), vrows = tensor_rows(a, a.v, bh);
+  const Rows kbrows = centroid_rows<T, D>(a, a.kbt, bh), vbrows = centroid_rows<T, D>(a, a.vbt, bh);
+  const int nsub = a.topk * SPB;
+  const int ntile = nsub + a.nct;
+  const int32_t* myidx = a.idx + ((size_t)bh * a.n + i) * a.topk;
+  // first row of key tile u in its source (a sub-tile past the sequence reads as zeros)
+  auto tile_r0 = [&](int u) {
+    if (u < nsub) return min(max(myidx[u / SPB], 0), a.n - 1) * a.blk + (u % SPB) * 64;
+    return 64 * (u - nsub);
+  };
+  uint4 pk[PER], pv[PER];
+  auto prefetch = [&](int u, bool values) {
+    const int k0 = tile_r0(u);
+    load_rows<T, D>(u < nsub ? krows : kbrows, k0, pk);
+    if (values) load_rows<T, D>(u < nsub ? vrows : vbrows, k0, pv);
+  };
+  // weight of each key of tile u: 1 for a token, n_j for an unselected
+  // centroid, -1 for no key (past the sequence, padding, selected centroid)
+  auto set_weights = [&](int u) {
+    if (tid >= 64) return;
+    if (u < nsub) {
+      wx_s[tid] = tile_r0(u) + tid < a.L ? 1.0f : -1.0f;
+    } else {
+      const int j = 64 * (u - nsub) + tid;
+      const bool sel = j < a.n && ((selw[j >> 5] >> (j & 31)) & 1u);
+      wx_s[tid] = (j < a.n && !sel) ? (float)(j == a.n - 1 ? a.n_last : a.blk) : -1.0f;
+    }
+  };
+
+  prefetch(0, false);
+  {
+    uint4 pq[PER], po[PER];
+    load_rows<T, D>(tensor_rows(a, a.q, bh), r0, pq);
+    load_rows<T, D>(tensor_rows(a, a.dout, bh), r0, po);
+    store_rows<T, D>(qt, pq);
+    store_rows<T, D>(ot, po);
+  }
   for (int x = tid; x < a.W; x += 256) selw[x] = a.selmap[((size_t)bh * a.n + i) * a.W + x];
   {  // Δ_t = dO_t·o_t, four threads per row
     const int row = tid >> 2, part = tid & 3, g = r0 + row;
@@ -188,42 +231,16 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
     acc += __shfl_xor(acc, 2);
     if (part == 0) dl_s[row] = acc;
   }
-  __syncthreads();
-
-  // the key tiles of this query tile: the selected blocks' 64-key sub-tiles,
-  // then the centroid tiles
-  const int nsub = a.topk * SPB;
-  const int ntile = nsub + a.nct;
-  const int32_t* myidx = a.idx + ((size_t)bh * a.n + i) * a.topk;
-  // stages tile u; returns false for a sub-tile past the end of the sequence
-  auto stage = [&](int u, bool values) -> bool {
-    if (u < nsub) {
-      const int j = min(max(myidx[u / SPB], 0), a.n - 1), st = u % SPB;
-      const int k0 = j * a.blk + st * 64;
-      if (k0 >= a.L) return false;
-      stage_rows<T, D>(kt, a.k, a, bh, k0);
-      if (values) stage_rows<T, D>(vt, a.v, a, bh, k0);
-      if (tid < 64) wx_s[tid] = k0 + tid < a.L ? 1.0f : -1.0f;
-    } else {
-      const int ct = u - nsub;
-      stage_stat<T, D>(kt, a.kbar, a, bh, ct);
-      if (values) stage_stat<T, D>(vt, a.vsum, a, bh, ct);
-      if (tid < 64) {
-        const int j = 64 * ct + tid;
-        const bool sel = j < a.n && ((selw[j >> 5] >> (j & 31)) & 1u);
-        wx_s[tid] = (j < a.n && !sel) ? (float)(j == a.n - 1 ? a.n_last : a.blk) : -1.0f;
-      }
-    }
-    return true;
-  };
 
   // ---- sweep 1: log2 D_t with an online maximum (per lane: column t)
   float m = -kInf, l = 0.0f;
   for (int u = 0; u < ntile; ++u) {
     __syncthreads();  // tiles free
-    const bool live = stage(u, false);
+    store_rows<T, D>(kt, pk);
+    set_weights(u);
     __syncthreads();
-    if (!live) continue;
+    if (u + 1 < ntile) prefetch(u + 1, false);
+    else prefetch(0, true);  // the first tile of the second sweep
     f32x16 sacc = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) Op<T>::mma(sacc, op_row<T, D>(kt, xh, c, lane), op_row<T, D>(qt, th, c, lane));
@@ -269,9 +286,11 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16{};
   for (int u = 0; u < ntile; ++u) {
     __syncthreads();
-    const bool live = stage(u, true);
+    store_rows<T, D>(kt, pk);
+    store_rows<T, D>(vt, pv);
+    set_weights(u);
     __syncthreads();
-    if (!live) continue;
+    if (u + 1 < ntile) prefetch(u + 1, true);
     f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -313,13 +332,18 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
 // quadrant of row half th x key half xh; its dk / dv partial covers keys xh
 // and sums rows th. CENT: a tile of 64 centroids, gradients of k̄ and ΣV (fp32,
 // to the workspace); otherwise a 64-key sub-tile of block j, whose final dk,
-// dv take the centroid gradients of j too.
+// dv take the centroid gradients of j too. The query blocks visited (those
+// that select block j; for centroids, those that leave one of the tile's
+// centroids out) are listed first, ascending, so the rows of the next query
+// tile load into registers while the current one is computed.
 template <typename T, int D, int SPB, bool CENT>
 __global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdArgs a) {
   using B = BT<T, D>;
-  constexpr int KW = B::KW, NC = B::NC, DT = B::DT, CPK = B::CPK;
+  constexpr int KW = B::KW, NC = B::NC, DT = B::DT, CPK = B::CPK, PER = B::PER;
   __shared__ __align__(16) uint8_t tiles[4 * B::TILE];  // k, v, q, dO; partial sums at the end
   __shared__ float lse_s[64], dl_s[64], wx_s[64];
+  __shared__ uint16_t qlist[kMaxBlocks];
+  __shared__ int qcount;
   uint8_t* kt = tiles;
   uint8_t* vt = tiles + B::TILE;
   uint8_t* qt = tiles + 2 * B::TILE;
@@ -342,39 +366,80 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdArgs a) {
     k0 = j * a.blk + st * 64;
     if (k0 >= a.L) return;
   }
-
-  if constexpr (CENT) {
-    stage_stat<T, D>(kt, a.kbar, a, bh, ct);
-    stage_stat<T, D>(vt, a.vsum, a, bh, ct);
-    if (tid < 64) {
-      const int jc = 64 * ct + tid;
-      wx_s[tid] = jc < a.n ? (float)(jc == a.n - 1 ? a.n_last : a.blk) : -1.0f;
-    }
-  } else {
-    stage_rows<T, D>(kt, a.k, a, bh, k0);
-    stage_rows<T, D>(vt, a.v, a, bh, k0);
-    if (tid < 64) wx_s[tid] = k0 + tid < a.L ? 1.0f : -1.0f;
-  }
   // centroids that exist in this tile (bit x: centroid 64 ct + x)
   const int nvalid_c = CENT ? min(64, a.n - 64 * ct) : 64;
   const unsigned long long valid_c = nvalid_c >= 64 ? ~0ull : ((1ull << nvalid_c) - 1ull);
+
+  // the query blocks to visit, ascending (wavefront 0)
+  if (w == 0) {
+    int cnt = 0;
+    for (int ib = 0; ib < a.n; ib += 64) {
+      const int i = ib + lane;
+      bool take = false;
+      if (i < a.n) {
+        if constexpr (CENT) take = (selected64(a, bh, i, ct) & valid_c) != valid_c;
+        else take = selected(a, bh, i, j);
+      }
+      const unsigned long long bits = __ballot(take);
+      if (take) qlist[cnt + __popcll(bits & ((1ull << lane) - 1ull))] = (uint16_t)i;
+      cnt += __popcll(bits);
+    }
+    if (lane == 0) qcount = cnt;
+  }
+  {
+    uint4 pk[PER], pv[PER];
+    const Rows kr = CENT ? centroid_rows<T, D>(a, a.kbt, bh) : tensor_rows(a, a.k, bh);
+    const Rows vr = CENT ? centroid_rows<T, D>(a, a.vbt, bh) : tensor_rows(a, a.v, bh);
+    const int kr0 = CENT ? 64 * ct : k0;
+    load_rows<T, D>(kr, kr0, pk);
+    load_rows<T, D>(vr, kr0, pv);
+    store_rows<T, D>(kt, pk);
+    store_rows<T, D>(vt, pv);
+  }
+  if (tid < 64) {
+    if constexpr (CENT) {
+      const int jc = 64 * ct + tid;
+      wx_s[tid] = jc < a.n ? (float)(jc == a.n - 1 ? a.n_last : a.blk) : -1.0f;
+    } else {
+      wx_s[tid] = k0 + tid < a.L ? 1.0f : -1.0f;
+    }
+  }
+  __syncthreads();
+  const int nitems = qcount * SPB;
 
   f32x16 dk[DT], dv[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dk[dt] = dv[dt] = f32x16{};
 
-  // one 64-row query tile against the key tile; cmask: centroids the query
-  // block selects (they take no weight from its rows)
-  auto query_tile = [&](int r0, unsigned long long cmask) {
-    __syncthreads();  // q / dO tiles free
-    stage_rows<T, D>(qt, a.q, a, bh, r0);
-    stage_rows<T, D>(ot, a.dout, a, bh, r0);
+  const Rows qrows = tensor_rows(a, a.q, bh), orows = tensor_rows(a, a.dout, bh);
+  const size_t row_base = (size_t)bh * a.n * a.blk;
+  uint4 pq[PER], po[PER];
+  float plse = kInf, pdl = 0.0f;
+  unsigned long long pcm = 0ull;
+  // item e: query block qlist[e / SPB], 64-row half e % SPB
+  auto prefetch = [&](int e) {
+    const int i = qlist[e / SPB], r0 = i * a.blk + (e % SPB) * 64;
+    load_rows<T, D>(qrows, r0, pq);
+    load_rows<T, D>(orows, r0, po);
     if (tid < 64) {
       const int g = r0 + tid;
-      lse_s[tid] = g < a.L ? a.lse[(size_t)bh * a.n * a.blk + g] : kInf;
-      dl_s[tid] = g < a.L ? a.delta[(size_t)bh * a.n * a.blk + g] : 0.0f;
+      plse = g < a.L ? a.lse[row_base + g] : kInf;  // rows past the sequence take no weight
+      pdl = g < a.L ? a.delta[row_base + g] : 0.0f;
     }
+    if constexpr (CENT) pcm = selected64(a, bh, i, ct);
+  };
+  if (nitems > 0) prefetch(0);
+  for (int e = 0; e < nitems; ++e) {
+    __syncthreads();  // q / dO tiles free
+    store_rows<T, D>(qt, pq);
+    store_rows<T, D>(ot, po);
+    if (tid < 64) {
+      lse_s[tid] = plse;
+      dl_s[tid] = pdl;
+    }
+    const unsigned long long cmask = pcm;  // centroids the query block selects: no weight
     __syncthreads();
+    if (e + 1 < nitems) prefetch(e + 1);
     f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -393,37 +458,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdArgs a) {
     }
 #pragma unroll
     for (int c = 0; c < CPK; ++c) {
-      const uint4 pv = Op<T>::pack(&p[KW * c]);
+      const uint4 pvv = Op<T>::pack(&p[KW * c]);
       const uint4 dsv = Op<T>::pack(&ds[KW * c]);
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        Op<T>::mma(dv[dt], pv, op_col<T, D>(ot, th, dt, c, lane));
+        Op<T>::mma(dv[dt], pvv, op_col<T, D>(ot, th, dt, c, lane));
         Op<T>::mma(dk[dt], dsv, op_col<T, D>(qt, th, dt, c, lane));
-      }
-    }
-  };
-
-  if constexpr (CENT) {
-    for (int i = 0; i < a.n; ++i) {
-      const unsigned long long cm = selected64(a, bh, i, ct);
-      if ((cm & valid_c) == valid_c) continue;  // the block selects every centroid here
-      for (int hf = 0; hf < SPB; ++hf) {
-        const int r0 = i * a.blk + hf * 64;
-        if (r0 < a.L) query_tile(r0, cm);
-      }
-    }
-  } else {
-    // the query blocks that select block j, ascending, 64 at a time
-    for (int ib = 0; ib < a.n; ib += 64) {
-      const int i = ib + lane;
-      unsigned long long bits = __ballot(i < a.n && selected(a, bh, i, j));
-      while (bits) {
-        const int ii = ib + __ffsll(bits) - 1;
-        bits &= bits - 1ull;
-        for (int hf = 0; hf < SPB; ++hf) {
-          const int r0 = ii * a.blk + hf * 64;
-          if (r0 < a.L) query_tile(r0, 0ull);
-        }
       }
     }
   }
@@ -437,15 +477,15 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdArgs a) {
   for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int x = 32 * xh + vkey(r, h), d = 32 * dt + l32;
+      const int xx = 32 * xh + vkey(r, h), d = 32 * dt + l32;
       if constexpr (CENT) {
-        const int jc = 64 * ct + x;
+        const int jc = 64 * ct + xx;
         if (jc < a.n) {
           a.dkbar[((size_t)bh * a.n + jc) * D + d] = a.scale * dk[dt][r];
           a.dvsum[((size_t)bh * a.n + jc) * D + d] = dv[dt][r];
         }
       } else {
-        const int g = k0 + x;
+        const int g = k0 + xx;
         if (g < a.L) {
           const float nj = (float)(j == a.n - 1 ? a.n_last : a.blk);
           const size_t sidx = ((size_t)bh * a.n + j) * D + d;
@@ -456,6 +496,20 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdArgs a) {
         }
       }
     }
+}
+
+// k̄_j and ΣV_j as rows in the I/O dtype (zero past n), for the centroid tiles.
+template <typename T, int D>
+__global__ void k_bwd_prep(BwdArgs a, long rows) {
+  for (long x = (long)blockIdx.x * 256 + threadIdx.x; x < rows * D; x += (long)gridDim.x * 256) {
+    const long r = x / D;
+    const int d = (int)(x % D);
+    const long bh = r / (a.nct * 64);
+    const int j = (int)(r % (a.nct * 64));
+    const size_t src = ((size_t)bh * a.n + j) * D + d;
+    ((T*)a.kbt)[x] = Op<T>::from_f32(j < a.n ? (float)a.kbar[src] : 0.0f);
+    ((T*)a.vbt)[x] = Op<T>::from_f32(j < a.n ? (float)a.vsum[src] : 0.0f);
+  }
 }
 
 // Selection bitmap: zeroed, then bit j of row i set for each selected block.
@@ -478,6 +532,9 @@ hipError_t launch_bwd_t(const BwdArgs& a, long bh, hipStream_t s) {
   const size_t words = (size_t)bh * a.n * a.W;
   hipLaunchKernelGGL(k_bwd_selmap_clear, dim3(1024), dim3(256), 0, s, a.selmap, words);
   hipLaunchKernelGGL(k_bwd_selmap_set, dim3((unsigned)(bh * a.n)), dim3(256), 0, s, a);
+  const long crow = bh * a.nct * 64;
+  hipLaunchKernelGGL((k_bwd_prep<T, D>), dim3((unsigned)min(4096L, (crow * D + 255) / 256)), dim3(256), 0, s, a,
+                     crow);
   hipLaunchKernelGGL((k_bwd_dq<T, D, SPB>), dim3((unsigned)(bh * a.n * SPB)), dim3(256), 0, s, a);
   hipLaunchKernelGGL((k_bwd_dkv<T, D, SPB, true>), dim3((unsigned)(bh * a.nct)), dim3(256), 0, s, a);
   hipLaunchKernelGGL((k_bwd_dkv<T, D, SPB, false>), dim3((unsigned)(bh * a.n * SPB)), dim3(256), 0, s, a);

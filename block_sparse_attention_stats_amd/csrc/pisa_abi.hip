@@ -397,6 +397,10 @@ pisa::BwdLayout bwd_layout(const pisa_shape_t* s, const pisa::WsLayout& w) {
   off = align256(off + (size_t)w.bh * w.n * s->D * sizeof(float));
   b.dvsum = off;
   off = align256(off + (size_t)w.bh * w.n * s->D * sizeof(float));
+  b.kbt = off;
+  off = align256(off + (size_t)w.bh * w.nct * 64 * s->D * w.esz);
+  b.vbt = off;
+  off = align256(off + (size_t)w.bh * w.nct * 64 * s->D * w.esz);
   b.total = off;
   return b;
 }
@@ -447,6 +451,8 @@ PISA_API pisa_status_t pisa_attn_bwd(const pisa_shape_t* shape, const void* q, c
   a.delta = (float*)(base + bl.delta);
   a.dkbar = (float*)(base + bl.dkbar);
   a.dvsum = (float*)(base + bl.dvsum);
+  a.kbt = base + bl.kbt;
+  a.vbt = base + bl.vbt;
   a.L = shape->L;
   a.n = w.n;
   a.blk = shape->block;

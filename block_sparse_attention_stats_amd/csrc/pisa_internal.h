@@ -88,13 +88,14 @@ struct BwdArgs {
   uint32_t* selmap;           // [BH][n][W]: bit j of row i set when query block i selects j
   float *lse, *delta;         // [BH][n*blk]: log2 of each row's denominator, dO·o
   float *dkbar, *dvsum;       // [BH][n][D]: gradients of k̄_j and ΣV_j
+  uint8_t *kbt, *vbt;         // [BH][nct*64][D]: k̄_j and ΣV_j in the I/O dtype, zero past n
   int L, n, blk, n_last, nct, topk, W;
   float scale;
 };
 
 // Byte offsets of the backward workspace regions (all 256-aligned).
 struct BwdLayout {
-  size_t selmap, lse, delta, dkbar, dvsum, total;
+  size_t selmap, lse, delta, dkbar, dvsum, kbt, vbt, total;
 };
 
 enum StatsMode { kStatsFull = 0, kStatsMnorm = 1, kStatsPackOnly = 2 };
