@@ -34,6 +34,35 @@ def _compile(src: str) -> str:
     return out
 
 
+SAN_LIB = os.path.join(OBJ, "san", "libpisa_san.so")
+# host code of the C ABI under AddressSanitizer and UndefinedBehaviorSanitizer
+# (the device code is built as usual: sanitizers apply to the host pass only)
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
+
+
+def build_host_sanitized(objs, verbose: bool = False) -> str:
+    """A copy of the library whose ABI layer (argument validation, workspace
+    layout, launch order: pisa_abi.hip) is compiled with host sanitizers and
+    linked to the regular kernel objects; tests/test_abi_sanitized.py runs the
+    host-side ABI checks through it."""
+    os.makedirs(os.path.dirname(SAN_LIB), exist_ok=True)
+    obj = os.path.join(OBJ, "san", "pisa_abi.o")
+    cmd = [HIPCC, *FLAGS, "-O1", "-g", *SAN_FLAGS, "-c", os.path.join(CSRC, "pisa_abi.hip"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the sanitized ABI layer:\n{r.stderr}")
+    kernels = [o for o in objs if not o.endswith("pisa_abi.hip.o")]
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address",
+           "-Xarch_host", "-fsanitize=undefined", "-shared-libasan", *kernels, obj, "-o", SAN_LIB]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed for the sanitized library:\n{r.stderr}")
+    if verbose:
+        print("built", SAN_LIB)
+    return SAN_LIB
+
+
 C_CALLER_SRC = os.path.join(ROOT, "tests", "c_abi", "pisa_c_caller.c")
 C_CALLER = os.path.join(ROOT, "tests", "c_abi", "pisa_c_caller")
 
@@ -68,6 +97,7 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print("built", LIB)
     build_c_caller(verbose)
+    build_host_sanitized(objs, verbose)
     return LIB
 
 
