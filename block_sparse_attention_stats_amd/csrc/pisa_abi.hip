@@ -18,6 +18,18 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Heads whose routing scores one pass of pisa_select holds: enough for about
+// 2048 workgroups of the score kernel (128 x 128 score tiles from 512 blocks
+// on, 64 x 64 below), at most all of them. The score buffer is sized for one
+// such chunk: about 2048 x 128² fp64 values (256 MiB) at most once n reaches
+// 512 blocks, whatever the head count (one head's n² scores when that alone is
+// more). At the Wan shape two chunks of 20 heads.
+long route_chunk(long bh, long n) {
+  const long t = n >= 512 ? (n + 127) / 128 : (n + 63) / 64;
+  const long c = (2048 + t * t - 1) / (t * t);
+  return c < 1 ? 1 : (c > bh ? bh : c);
+}
+
 // Validates the shape; fills the workspace layout. Returns PISA_OK or the error.
 pisa_status_t check_shape(const pisa_shape_t* s, pisa::WsLayout* w) {
   if (s == nullptr) return PISA_EINVAL;
@@ -66,7 +78,7 @@ pisa_status_t check_shape(const pisa_shape_t* s, pisa::WsLayout* w) {
   w->hpart = off;
   off = align256(off + (size_t)bh * w->nch * s->D * s->D * sizeof(float));
   w->scores = off;
-  off = align256(off + (size_t)bh * n * n * sizeof(double));
+  off = align256(off + (size_t)route_chunk(bh, n) * n * n * sizeof(double));
   w->total = off;
   return PISA_OK;
 }
@@ -322,14 +334,24 @@ PISA_API pisa_status_t pisa_select(const pisa_shape_t* shape, const pisa_stats_t
   sa.cov_weight = cov_weight;
   sa.n = w.n;
   sa.sink_block = sink_idx == PISA_SINK_NONE ? -1 : (sink_idx == 0 ? 0 : w.n - 1);
-  if (topk < w.n)
-    if ((rc = hip_status(pisa::launch_scores(shape->D, sa, w.bh, s)))) return rc;
   pisa::TopkArgs ta;
   ta.scores = sa.scores;
-  ta.idx = idx;
   ta.n = w.n;
   ta.topk = topk;
-  return hip_status(pisa::launch_topk(ta, w.bh * w.n, s));
+  // heads in chunks that share one score buffer (stream order keeps them apart)
+  const long chunk = route_chunk(w.bh, w.n);
+  for (long h0 = 0; h0 < w.bh; h0 += chunk) {
+    const long hc = w.bh - h0 < chunk ? w.bh - h0 : chunk;
+    pisa::ScoreArgs sc = sa;
+    sc.qbar = st->qbar + (size_t)h0 * w.n * shape->D;
+    sc.kbar = st->kbar + (size_t)h0 * w.n * shape->D;
+    sc.mnorm = st->mnorm ? st->mnorm + (size_t)h0 * w.n : nullptr;
+    if (topk < w.n)
+      if ((rc = hip_status(pisa::launch_scores(shape->D, sc, hc, s)))) return rc;
+    ta.idx = idx + (size_t)h0 * w.n * topk;
+    if ((rc = hip_status(pisa::launch_topk(ta, hc * w.n, s)))) return rc;
+  }
+  return PISA_OK;
 }
 
 PISA_API pisa_status_t pisa_attn_fwd_seg(const pisa_shape_t* shape, const void* q,

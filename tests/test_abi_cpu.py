@@ -168,3 +168,15 @@ def test_noalloc_arguments_rejected_on_the_host():
     assert call(s=shape(H=8, L=75600)) == bsa.PISA_ETOOBIG
     assert call(s=shape(H=40, L=75600)) == bsa.PISA_ETOOBIG
     assert lib.pisa_status_string(bsa.PISA_ETOOBIG).decode().startswith("problem larger")
+
+
+def test_routing_scores_do_not_grow_with_heads():
+    """pisa_select runs the heads in chunks over one score buffer: at the Wan
+    shape (1182 blocks, 11 MB of fp64 scores per head) 80 more heads add their
+    K/V copies and statistics (about 44 MB each) but no score matrices."""
+    lib = bsa.load_library()
+    ws = lambda H: lib.pisa_workspace_bytes(ctypes.byref(shape(H=H, L=75600)))
+    per_head = (ws(120) - ws(40)) / 80
+    n = 1182
+    assert 40e6 < per_head < 40e6 + n * n * 8 / 2
+    assert ws(40) < 40 * 46e6 + 21 * n * n * 8
