@@ -37,9 +37,9 @@ HBM_PEAK_GBS = 8000.0
 # is kept, and the figure is reported as null once the sources differ.
 FUSED_TRAFFIC = {"workload": "wan_bf16",
                  "sources": ["k_fwd.hip", "pisa_dev.h", "pisa_internal.h", "pisa_abi.hip"],
-                 "sha1": "159ada07f3ba4c2f023749888b6d28ca1ff9f9f4",
-                 "fetch_kib": (37460846.375 + 37829795.625) / 2, "fetch_scale": 2.0,
-                 "write_kib": (757478.4062 + 757480.0312) / 2, "write_scale": 1.0}
+                 "sha1": "c27f9f0cc59c16a5ae680aebca314e82e05e20f5",
+                 "fetch_kib": (27186758.5 + 27534844.1) / 2, "fetch_scale": 2.0,
+                 "write_kib": (757478.0 + 757478.5) / 2, "write_scale": 1.0}
 
 
 def fused_traffic(workload: str):
@@ -214,6 +214,8 @@ def main():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="wan_bf16")
+    ap.add_argument("--cov-norm", choices=["fro", "spectral"], default=None,
+                    help="norm of the covariance term of the workload's routing (default: its own)")
     ap.add_argument("--dense-reps", type=int, default=2)
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--pb1-reps", type=int, default=2,
@@ -259,6 +261,8 @@ def main():
         return
 
     w = synth.WORKLOADS[args.workload]
+    if args.cov_norm:
+        w = w.replace(cov_norm=args.cov_norm)
     t0 = time.time()
     print(f"[bench] generating {w.name} inputs", file=sys.stderr, flush=True)
     q, k, v = synth.make_qkv(w)
@@ -278,7 +282,7 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record()
-        bsa.block_stats(qd, kd, vd, w.block, want_mnorm=w.cov_weight > 0, out=st)
+        bsa.block_stats(qd, kd, vd, w.block, want_mnorm=w.cov_weight > 0, out=st, cov_norm=w.cov_norm)
         if ev is not None:
             ev[1].record()
         bsa.select(st, topk, s, w.cov_weight, w.sink_idx, out=idx)
@@ -429,7 +433,7 @@ def main():
         "data": "synthetic: seeded clustered-Gaussian q/k (64-token clusters), N(0,1) v",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "L": w.L, "D": w.D, "block": w.block,
                    "density": w.density, "topk": topk, "variant": w.variant, "sink_idx": w.sink_idx,
-                   "cov_weight": w.cov_weight, "seed": w.seed},
+                   "cov_weight": w.cov_weight, "cov_norm": w.cov_norm, "seed": w.seed},
         "ms": ms,
         "flops": f,
         "fused_tflops": fused_tflops,
