@@ -367,15 +367,16 @@ def main():
         # selection, with a seeded upstream gradient of the output's shape
         gen = torch.Generator(device=dev).manual_seed(w.seed)
         dout = torch.randn(qd.shape, generator=gen, device=dev, dtype=torch.float32).to(qd.dtype)
-        o0 = bsa.attn_fwd(qd, st, idx, s, "0th")
+        # the forward hands ln D_t to the backward, as the autograd path does
+        o0, lse0 = bsa.attn_fwd(qd, st, idx, s, "0th", return_lse=True)
         bws = torch.empty(bsa.load_library().pisa_bwd_workspace_bytes(bsa.ctypes.byref(shape)),
                           dtype=torch.uint8, device=dev)
-        bsa.attn_bwd(qd, kd, vd, st, idx, s, o0, dout, ws=bws)
+        bsa.attn_bwd(qd, kd, vd, st, idx, s, o0, dout, ws=bws, lse=lse0)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(args.bwd_reps):
-            bsa.attn_bwd(qd, kd, vd, st, idx, s, o0, dout, ws=bws)
+            bsa.attn_bwd(qd, kd, vd, st, idx, s, o0, dout, ws=bws, lse=lse0)
         e1.record()
         torch.cuda.synchronize()
         bwd_ms = e0.elapsed_time(e1) / args.bwd_reps
@@ -386,7 +387,7 @@ def main():
                "mfma_frac": bflops / (bwd_ms * 1e-3) / 1e12 / peak,
                "ms_vs_fwd_fused": bwd_ms / ms["attn_fwd"]}
         print(f"[bench] backward (0th) {bwd_ms:.2f} ms, {bwd['tflops']:.1f} TFLOP/s", file=sys.stderr, flush=True)
-        del dout, o0, bws
+        del dout, o0, lse0, bws
 
     banded = None
     if not args.no_banded:

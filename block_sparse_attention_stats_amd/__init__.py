@@ -34,7 +34,7 @@ PISA_SINK_NONE = -(2 ** 31)
 EXPORTS = ("pisa_workspace_bytes", "pisa_block_stats", "pisa_select", "pisa_attn_fwd",
            "dense_workspace_bytes", "dense_attn_fwd", "pisa_status_string", "pisa_last_hip_error",
            "pisa_block_stats_seg", "pisa_attn_fwd_seg", "dense_attn_fwd_seg", "pisa_attn_fwd_noalloc",
-           "pisa_bwd_workspace_bytes", "pisa_attn_bwd")
+           "pisa_bwd_workspace_bytes", "pisa_attn_bwd", "pisa_attn_fwd_lse")
 
 
 class PisaError(RuntimeError):
@@ -96,13 +96,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "pisa_block_stats": (I32, [SP, P, P, P, STP, P]),
         "pisa_select": (I32, [SP, STP, D64, D64, I32, I32, P, P]),
         "pisa_attn_fwd": (I32, [SP, P, STP, I32, P, I32, D64, P, P]),
+        "pisa_attn_fwd_lse": (I32, [SP, P, STP, I32, P, I32, D64, P, P, P]),
         "dense_attn_fwd": (I32, [SP, P, P, P, D64, P, P, SZ, P]),
         "pisa_block_stats_seg": (I32, [SP, P, P, P, SG, STP, P]),
         "pisa_attn_fwd_seg": (I32, [SP, P, STP, I32, P, I32, D64, P, SG, P]),
         "dense_attn_fwd_seg": (I32, [SP, P, P, P, SG, D64, P, P, SZ, P]),
         "pisa_attn_fwd_noalloc": (I32, [SP, P, P, P, I32, P, I32, D64, P, P]),
         "pisa_bwd_workspace_bytes": (SZ, [SP]),
-        "pisa_attn_bwd": (I32, [SP, P, P, P, STP, P, I32, D64, P, P, P, P, P, P, SZ, P]),
+        "pisa_attn_bwd": (I32, [SP, P, P, P, STP, P, I32, D64, P, P, P, P, P, P, P, SZ, P]),
         "pisa_status_string": (ctypes.c_char_p, [I32]),
         "pisa_last_hip_error": (ctypes.c_char_p, []),
     }
@@ -351,11 +352,13 @@ def _variant_code(first_order) -> int:
 
 
 def attn_fwd(q, st: Stats, idx: torch.Tensor, scale: float, first_order=True,
-             out: torch.Tensor | None = None) -> torch.Tensor:
+             out: torch.Tensor | None = None, return_lse: bool = False):
     """Step 3: fused exact + zeroth-order (+ first-order) pass.
 
     first_order: True or "hyd" (global H̄ term), False or "0th" (none), "pb1"
-    (each unselected block's own first-order term)."""
+    (each unselected block's own first-order term). With return_lse the call
+    goes through pisa_attn_fwd_lse and returns (o, lse), lse [B,H,L] fp32 =
+    ln D_t of each row, which attn_bwd can take."""
     code = _variant_code(first_order)
     shape = st.shape
     st.check()
@@ -366,10 +369,15 @@ def attn_fwd(q, st: Stats, idx: torch.Tensor, scale: float, first_order=True,
     _on_gpu(q, idx, *st.tensors(), *(() if out is None else (out,)))
     o = out if out is not None else torch.empty_like(q)
     sst = st.struct()
-    _check(load_library().pisa_attn_fwd(ctypes.byref(shape), q.data_ptr(), ctypes.byref(sst),
-                                        code, idx.data_ptr(), topk,
-                                        float(scale), o.data_ptr(), _stream()), "pisa_attn_fwd")
-    return o
+    lib = load_library()
+    if not return_lse:
+        _check(lib.pisa_attn_fwd(ctypes.byref(shape), q.data_ptr(), ctypes.byref(sst), code, idx.data_ptr(),
+                                 topk, float(scale), o.data_ptr(), _stream()), "pisa_attn_fwd")
+        return o
+    lse = torch.empty((shape.B, shape.H, shape.L), dtype=torch.float32, device=q.device)
+    _check(lib.pisa_attn_fwd_lse(ctypes.byref(shape), q.data_ptr(), ctypes.byref(sst), code, idx.data_ptr(),
+                                 topk, float(scale), o.data_ptr(), lse.data_ptr(), _stream()), "pisa_attn_fwd_lse")
+    return o, lse
 
 
 def attn_fwd_noalloc(q, k, v, idx: torch.Tensor, scale: float, first_order=True, block_size: int = 64,
@@ -393,29 +401,36 @@ def attn_fwd_noalloc(q, k, v, idx: torch.Tensor, scale: float, first_order=True,
     return o
 
 
-def attn_bwd(q, k, v, st: Stats, idx: torch.Tensor, scale: float, o, dout, ws: torch.Tensor | None = None):
+def attn_bwd(q, k, v, st: Stats, idx: torch.Tensor, scale: float, o, dout, ws: torch.Tensor | None = None,
+             lse: torch.Tensor | None = None):
     """Backward pass of the zeroth-order-only variant via pisa_attn_bwd: the
     gradients (dq, dk, dv) of Σ o∘dout, with the selection idx held fixed. q,
-    k, v, st and idx are those of the forward call and o its output."""
+    k, v, st and idx are those of the forward call and o its output; lse, if
+    given, the ln D_t that the forward returned (attn_fwd(..., return_lse=True)),
+    which saves the backward a sweep."""
     _check_qkv(q, k, v)
     shape = st.shape
     st.check()
     for t, name in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (dout, "dout")):
         _check_io(t, shape, name)
     topk = _check_idx(idx, shape)
+    if lse is not None:
+        _expect(lse, (shape.B, shape.H, shape.L), torch.float32, "lse")
     lib = load_library()
     nbytes = lib.pisa_bwd_workspace_bytes(ctypes.byref(shape))
     if nbytes == 0:
         raise PisaError(PISA_EINVAL, "pisa_bwd_workspace_bytes")
     if ws is not None and (ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous()):
         raise ValueError("ws must be a contiguous 1-D uint8 tensor")
-    _on_gpu(q, k, v, o, dout, idx, *st.tensors(), *(() if ws is None else (ws,)))
+    _on_gpu(q, k, v, o, dout, idx, *st.tensors(), *(() if ws is None else (ws,)),
+            *(() if lse is None else (lse,)))
     if ws is None or ws.numel() < nbytes:
         ws = torch.empty(nbytes, dtype=torch.uint8, device=q.device)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     sst = st.struct()
     _check(lib.pisa_attn_bwd(ctypes.byref(shape), q.data_ptr(), k.data_ptr(), v.data_ptr(), ctypes.byref(sst),
-                             idx.data_ptr(), topk, float(scale), o.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                             idx.data_ptr(), topk, float(scale), o.data_ptr(),
+                             None if lse is None else lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
                              dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream()),
            "pisa_attn_bwd")
     return dq, dk, dv
@@ -433,16 +448,16 @@ class _Pisa0th(torch.autograd.Function):
         topk = topk_from_density(density, num_blocks(shape.L, block_size))
         st = block_stats(q, k, v, block_size, want_mnorm=cov_weight > 0, layout=layout, cov_norm=cov_norm)
         idx = select(st, topk, s, cov_weight, sink_idx)
-        o = attn_fwd(q, st, idx, s, False)
-        ctx.save_for_backward(q, k, v, o, idx)
+        o, lse = attn_fwd(q, st, idx, s, False, return_lse=True)
+        ctx.save_for_backward(q, k, v, o, idx, lse)
         ctx.st, ctx.scale = st, s
         ctx.mark_non_differentiable(idx)
         return o, idx
 
     @staticmethod
     def backward(ctx, do, _didx):
-        q, k, v, o, idx = ctx.saved_tensors
-        dq, dk, dv = attn_bwd(q, k, v, ctx.st, idx, ctx.scale, o, do.contiguous())
+        q, k, v, o, idx, lse = ctx.saved_tensors
+        dq, dk, dv = attn_bwd(q, k, v, ctx.st, idx, ctx.scale, o, do.contiguous(), lse=lse)
         return dq, dk, dv, None, None, None, None, None, None, None
 
 

@@ -23,7 +23,8 @@
 // gathered from the LDS tile by the same key order (vkey, pisa_dev.h).
 //   k_bwd_dq:  one workgroup per 64-row query tile: a first sweep over the
 //              selected sub-tiles and the centroid tiles gives log2 D_t (an
-//              online maximum), a second sweep dq; it stores log2 D_t and Δ_t.
+//              online maximum; skipped when the forward pass handed over
+//              ln D_t), a second sweep dq; it stores log2 D_t and Δ_t.
 //   k_bwd_dkv<centroid>: one workgroup per tile of 64 centroids, over every
 //              query tile whose block leaves one of them out: dk̄, dΣV.
 //   k_bwd_dkv<token>: one workgroup per 64-key sub-tile, over the query
@@ -38,6 +39,9 @@ namespace pisa {
 namespace {
 
 constexpr float kInf = __builtin_huge_valf();
+// Query blocks listed at a time by a key tile's workgroup: the list's LDS
+// stays small enough for two bf16 workgroups of k_bwd_dkv per compute unit.
+constexpr int kQChunk = 4096;
 
 template <typename T, int D>
 struct BT {
@@ -204,7 +208,9 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
     }
   };
 
-  prefetch(0, false);
+  // ln D_t from the forward pass makes the first sweep unnecessary
+  const bool have_lse = a.lse_in != nullptr;
+  prefetch(0, have_lse);
   {
     uint4 pq[PER], po[PER];
     load_rows<T, D>(tensor_rows(a, a.q, bh), r0, pq);
@@ -234,7 +240,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
 
   // ---- sweep 1: log2 D_t with an online maximum (per lane: column t)
   float m = -kInf, l = 0.0f;
-  for (int u = 0; u < ntile; ++u) {
+  for (int u = 0; u < (have_lse ? 0 : ntile); ++u) {
     __syncthreads();  // tiles free
     store_rows<T, D>(kt, pk);
     set_weights(u);
@@ -272,7 +278,8 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
     const float mm = fmaxf(m, m1);
     const float ll = l * __builtin_amdgcn_exp2f(m - mm) + l1 * __builtin_amdgcn_exp2f(m1 - mm);
     const int t = 32 * th + l32, g = r0 + t;
-    const float v2 = g < a.L ? mm + __log2f(ll) : kInf;  // padding rows: every weight 0
+    float v2 = kInf;  // padding rows: every weight 0
+    if (g < a.L) v2 = have_lse ? a.lse_in[(size_t)bh * a.L + g] * kLog2e : mm + __log2f(ll);
     lse_s[t] = v2;
     if (g < a.L) {
       a.lse[(size_t)bh * a.n * a.blk + g] = v2;
@@ -337,13 +344,13 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
 // centroids out) are listed first, ascending, so the rows of the next query
 // tile load into registers while the current one is computed.
 template <typename T, int D, int SPB, bool CENT>
-__global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdArgs a) {
+__global__ __launch_bounds__(256, 2) void k_bwd_dkv(BwdArgs a) {
   using B = BT<T, D>;
   constexpr int KW = B::KW, NC = B::NC, DT = B::DT, CPK = B::CPK, PER = B::PER;
   __shared__ __align__(16) uint8_t tiles[4 * B::TILE];  // k, v, q, dO; partial sums at the end
   __shared__ float lse_s[64], dl_s[64], wx_s[64];
-  __shared__ uint16_t qlist[kMaxBlocks];
-  __shared__ int qcount;
+  __shared__ uint16_t qlist[kQChunk];
+  __shared__ int qcount, qnext;
   uint8_t* kt = tiles;
   uint8_t* vt = tiles + B::TILE;
   uint8_t* qt = tiles + 2 * B::TILE;
@@ -370,10 +377,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdArgs a) {
   const int nvalid_c = CENT ? min(64, a.n - 64 * ct) : 64;
   const unsigned long long valid_c = nvalid_c >= 64 ? ~0ull : ((1ull << nvalid_c) - 1ull);
 
-  // the query blocks to visit, ascending (wavefront 0)
-  if (w == 0) {
-    int cnt = 0;
-    for (int ib = 0; ib < a.n; ib += 64) {
+  // the query blocks to visit, ascending, listed by wavefront 0 in chunks of
+  // at most kQChunk, the scan of query blocks resuming at `from`
+  auto list_chunk = [&](int from) {
+    if (w != 0) return;
+    int cnt = 0, ib = from;
+    for (; ib < a.n && cnt <= kQChunk - 64; ib += 64) {
       const int i = ib + lane;
       bool take = false;
       if (i < a.n) {
@@ -384,8 +393,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdArgs a) {
       if (take) qlist[cnt + __popcll(bits & ((1ull << lane) - 1ull))] = (uint16_t)i;
       cnt += __popcll(bits);
     }
-    if (lane == 0) qcount = cnt;
-  }
+    if (lane == 0) {
+      qcount = cnt;
+      qnext = ib;
+    }
+  };
+  list_chunk(0);
   {
     uint4 pk[PER], pv[PER];
     const Rows kr = CENT ? centroid_rows<T, D>(a, a.kbt, bh) : tensor_rows(a, a.k, bh);
@@ -405,7 +418,6 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdArgs a) {
     }
   }
   __syncthreads();
-  const int nitems = qcount * SPB;
 
   f32x16 dk[DT], dv[DT];
 #pragma unroll
@@ -428,44 +440,51 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dkv(BwdArgs a) {
     }
     if constexpr (CENT) pcm = selected64(a, bh, i, ct);
   };
-  if (nitems > 0) prefetch(0);
-  for (int e = 0; e < nitems; ++e) {
-    __syncthreads();  // q / dO tiles free
-    store_rows<T, D>(qt, pq);
-    store_rows<T, D>(ot, po);
-    if (tid < 64) {
-      lse_s[tid] = plse;
-      dl_s[tid] = pdl;
-    }
-    const unsigned long long cmask = pcm;  // centroids the query block selects: no weight
-    __syncthreads();
-    if (e + 1 < nitems) prefetch(e + 1);
-    f32x16 sacc = f32x16{}, pacc = f32x16{};
+  for (;;) {
+    const int nitems = qcount * SPB, from = qnext;
+    if (nitems > 0) prefetch(0);
+    for (int e = 0; e < nitems; ++e) {
+      __syncthreads();  // q / dO tiles free
+      store_rows<T, D>(qt, pq);
+      store_rows<T, D>(ot, po);
+      if (tid < 64) {
+        lse_s[tid] = plse;
+        dl_s[tid] = pdl;
+      }
+      const unsigned long long cmask = pcm;  // centroids the query block selects: no weight
+      __syncthreads();
+      if (e + 1 < nitems) prefetch(e + 1);
+      f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      Op<T>::mma(sacc, op_row<T, D>(qt, th, c, lane), op_row<T, D>(kt, xh, c, lane));
-      Op<T>::mma(pacc, op_row<T, D>(ot, th, c, lane), op_row<T, D>(vt, xh, c, lane));
-    }
-    const int x = 32 * xh + l32;
-    const float wx = wx_s[x];
-    const bool live = wx >= 0.0f && !((cmask >> x) & 1ull);
-    float p[16], ds[16];
+      for (int c = 0; c < NC; ++c) {
+        Op<T>::mma(sacc, op_row<T, D>(qt, th, c, lane), op_row<T, D>(kt, xh, c, lane));
+        Op<T>::mma(pacc, op_row<T, D>(ot, th, c, lane), op_row<T, D>(vt, xh, c, lane));
+      }
+      const int x = 32 * xh + l32;
+      const float wx = wx_s[x];
+      const bool live = wx >= 0.0f && !((cmask >> x) & 1ull);
+      float p[16], ds[16];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int t = 32 * th + vkey(r, h);
-      p[r] = live ? __builtin_amdgcn_exp2f(sacc[r] * cs - lse_s[t]) : 0.0f;
-      ds[r] = p[r] * (pacc[r] - wx * dl_s[t]);
-    }
+      for (int r = 0; r < 16; ++r) {
+        const int t = 32 * th + vkey(r, h);
+        p[r] = live ? __builtin_amdgcn_exp2f(sacc[r] * cs - lse_s[t]) : 0.0f;
+        ds[r] = p[r] * (pacc[r] - wx * dl_s[t]);
+      }
 #pragma unroll
-    for (int c = 0; c < CPK; ++c) {
-      const uint4 pvv = Op<T>::pack(&p[KW * c]);
-      const uint4 dsv = Op<T>::pack(&ds[KW * c]);
+      for (int c = 0; c < CPK; ++c) {
+        const uint4 pvv = Op<T>::pack(&p[KW * c]);
+        const uint4 dsv = Op<T>::pack(&ds[KW * c]);
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        Op<T>::mma(dv[dt], pvv, op_col<T, D>(ot, th, dt, c, lane));
-        Op<T>::mma(dk[dt], dsv, op_col<T, D>(qt, th, dt, c, lane));
+        for (int dt = 0; dt < DT; ++dt) {
+          Op<T>::mma(dv[dt], pvv, op_col<T, D>(ot, th, dt, c, lane));
+          Op<T>::mma(dk[dt], dsv, op_col<T, D>(qt, th, dt, c, lane));
+        }
       }
     }
+    if (from >= a.n) break;
+    __syncthreads();  // every thread has read qcount, qnext and its last list entry
+    list_chunk(from);
+    __syncthreads();
   }
 
   __syncthreads();  // tiles free: partial sums of the two row halves meet there

@@ -493,9 +493,10 @@ __device__ __forceinline__ void pipelined(int nt, const uint8_t* kbase, const ui
 }
 
 // Sums the two wavefronts' partial states (wavefront W finishes output tiles
-// W*DH .. W*DH+DH-1), adds the first-order term and stores o = N / D. In the
-// fast kernel a tile whose denominator is too small is queued for the careful
-// kernel and nothing is stored.
+// W*DH .. W*DH+DH-1), adds the first-order term and stores o = N / D (and, when
+// a.lse is set, ln D_t for a backward pass). In the fast kernel a tile whose
+// denominator is too small is queued for the careful kernel and nothing is
+// stored.
 template <typename T, int D, bool CAREFUL, int W>
 __device__ __forceinline__ void epilogue(const FwdArgs& a, typename Regs<T, D>::Acc& oacc,
                                          float (&m)[2], float (&l)[2], float (&asum)[2],
@@ -535,14 +536,20 @@ __device__ __forceinline__ void epilogue(const FwdArgs& a, typename Regs<T, D>::
     const float lp = sh.xstat[1 - w][1][qt][l32];
     const float ap = sh.xstat[1 - w][2][qt][l32];
     float fs = 1.0f, fp = 1.0f;  // the fast kernel's shift is the same in both wavefronts
+    float mt = m[qt];
     if constexpr (CAREFUL) {
       const float mstar = fmaxf(m[qt], mp);
       fs = (m[qt] == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(m[qt] - mstar);
       fp = (mp == kNegInf) ? 0.0f : __builtin_amdgcn_exp2f(mp - mstar);
+      mt = mstar;
     }
     Lt[qt] = fs * l[qt] + fp * lp;
     At[qt] = fs * asum[qt] + fp * ap;
     const int row = r0 + 32 * qt + l32;
+    // ln D_t = (shift + log2 of the shifted sum) · ln 2, when asked for (a
+    // tile the fast kernel hands to the careful kernel is written again there)
+    if (a.lse != nullptr && w == 0 && h == 0 && row < a.L)
+      a.lse[(size_t)bh * a.L + row] = (mt + __log2f(Lt[qt])) * kLn2;
     if (!CAREFUL && row < a.L && !(Lt[qt] >= kTinyDenom && Lt[qt] < __builtin_huge_valf())) tiny = true;
 #pragma unroll
     for (int t = 0; t < DH; ++t) {

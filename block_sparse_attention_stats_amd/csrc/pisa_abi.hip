@@ -207,6 +207,7 @@ pisa::FwdArgs fwd_args(const pisa_shape_t* s, const pisa::WsLayout& w, const voi
   a.o1 = (uint8_t*)(seg ? seg->o1 : nullptr);
   a.L0 = (int)L0;
   a.H = s->H;
+  a.lse = nullptr;
   return a;
 }
 
@@ -375,6 +376,21 @@ PISA_API pisa_status_t pisa_attn_fwd(const pisa_shape_t* shape, const void* q,
   return pisa_attn_fwd_seg(shape, q, st, first_order, idx, topk, scale, o, nullptr, stream);
 }
 
+PISA_API pisa_status_t pisa_attn_fwd_lse(const pisa_shape_t* shape, const void* q,
+                                         const pisa_stats_t* st, int32_t first_order,
+                                         const int32_t* idx, int32_t topk, double scale, void* o,
+                                         float* lse, void* stream) {
+  pisa::WsLayout w;
+  pisa_status_t rc = check_shape(shape, &w);
+  if (rc != PISA_OK) return rc;
+  if ((rc = check_fwd_args(w, q, o, first_order, idx, topk, scale)) != PISA_OK) return rc;
+  if (lse == nullptr || !aligned(lse, 4)) return PISA_EINVAL;
+  if ((rc = check_stats(st, w, false)) != PISA_OK) return rc;
+  pisa::FwdArgs a = fwd_args(shape, w, q, o, nullptr, st->ws, idx, topk, scale, first_order, 1);
+  a.lse = lse;
+  return hip_status(pisa::launch_fwd(shape->dtype, shape->D, a, (hipStream_t)stream));
+}
+
 PISA_API pisa_status_t pisa_attn_fwd_noalloc(const pisa_shape_t* shape, const void* q,
                                              const void* k, const void* v, int32_t first_order,
                                              const int32_t* idx, int32_t topk, double scale,
@@ -436,9 +452,9 @@ PISA_API size_t pisa_bwd_workspace_bytes(const pisa_shape_t* shape) {
 
 PISA_API pisa_status_t pisa_attn_bwd(const pisa_shape_t* shape, const void* q, const void* k,
                                      const void* v, const pisa_stats_t* st, const int32_t* idx,
-                                     int32_t topk, double scale, const void* o, const void* dout,
-                                     void* dq, void* dk, void* dv, void* ws, size_t ws_bytes,
-                                     void* stream) {
+                                     int32_t topk, double scale, const void* o, const float* lse,
+                                     const void* dout, void* dq, void* dk, void* dv, void* ws,
+                                     size_t ws_bytes, void* stream) {
   pisa::WsLayout w;
   pisa_status_t rc = check_shape(shape, &w);
   if (rc != PISA_OK) return rc;
@@ -448,6 +464,7 @@ PISA_API pisa_status_t pisa_attn_bwd(const pisa_shape_t* shape, const void* q, c
   if (!(scale > 0.0) || !isfinite(scale)) return PISA_EINVAL;
   if (topk < 1 || topk > w.n) return PISA_EINVAL;
   if (idx == nullptr || !aligned(idx, 4)) return PISA_EINVAL;
+  if (lse != nullptr && !aligned(lse, 4)) return PISA_EINVAL;
   if (st == nullptr || st->kbar == nullptr || st->vsum == nullptr || !aligned(st->kbar, 8) ||
       !aligned(st->vsum, 8))
     return PISA_EINVAL;
@@ -470,6 +487,7 @@ PISA_API pisa_status_t pisa_attn_bwd(const pisa_shape_t* shape, const void* q, c
   a.idx = idx;
   a.selmap = (uint32_t*)(base + bl.selmap);
   a.lse = (float*)(base + bl.lse);
+  a.lse_in = lse;
   a.delta = (float*)(base + bl.delta);
   a.dkbar = (float*)(base + bl.dkbar);
   a.dvsum = (float*)(base + bl.dvsum);

@@ -35,6 +35,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 constexpr int kWave = 64;   // wavefront width
 constexpr int kSub = 64;    // keys per packed sub-tile
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 
 // Key (0..31) held in accumulator register r by lane half h.
 __host__ __device__ constexpr int vkey(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }

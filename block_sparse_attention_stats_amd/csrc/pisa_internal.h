@@ -75,6 +75,7 @@ struct FwdArgs {
   uint8_t* o1;
   size_t stride1_b, stride1_h, stride1_l;
   int H, L0;
+  float* lse;  // [BH][L]: natural log of each row's denominator D_t, or nullptr
 };
 
 // Backward pass of the zeroth-order variant.
@@ -87,6 +88,7 @@ struct BwdArgs {
   const int32_t* idx;         // [BH][n][topk]
   uint32_t* selmap;           // [BH][n][W]: bit j of row i set when query block i selects j
   float *lse, *delta;         // [BH][n*blk]: log2 of each row's denominator, dO·o
+  const float* lse_in;        // [BH][L]: ln D_t from the forward pass, or nullptr
   float *dkbar, *dvsum;       // [BH][n][D]: gradients of k̄_j and ΣV_j
   uint8_t *kbt, *vbt;         // [BH][nct*64][D]: k̄_j and ΣV_j in the I/O dtype, zero past n
   int L, n, blk, n_last, nct, topk, W;

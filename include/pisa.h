@@ -174,6 +174,17 @@ pisa_status_t pisa_attn_fwd(const pisa_shape_t *shape, const void *q, const pisa
                             int32_t first_order, const int32_t *idx, int32_t topk, double scale,
                             void *o, void *stream);
 
+/* pisa_attn_fwd that also writes, for every row t, lse[t] = ln D_t: the
+ * natural log of the row's denominator D_t (the gist's "Core Algorithm", the
+ * same for all three variants up to rounding), taken over the unshifted
+ * exponentials e^{scale q_t·k}. lse is a caller-owned device buffer of
+ * [B,H,L] fp32 (4-byte aligned, in this order whatever shape->layout is).
+ * It is what pisa_attn_bwd can take instead of recomputing the denominators.
+ * Errors as for pisa_attn_fwd, and PISA_EINVAL for a NULL or misaligned lse. */
+pisa_status_t pisa_attn_fwd_lse(const pisa_shape_t *shape, const void *q, const pisa_stats_t *st,
+                                int32_t first_order, const int32_t *idx, int32_t topk, double scale,
+                                void *o, float *lse, void *stream);
+
 /* Backward pass of the zeroth-order-only variant (first_order = 0), the form
  * the README's "Kernel variants" names as the one that supports training.
  * With the selection idx held fixed, the gradients of L = Σ o∘dout follow from
@@ -185,6 +196,9 @@ pisa_status_t pisa_attn_fwd(const pisa_shape_t *shape, const void *q, const pisa
  *             workspace copies are not)
  *   idx, topk the forward's selection, as for pisa_attn_fwd
  *   o         the forward's output (o_t enters through Δ_t = dout_t·o_t)
+ *   lse       NULL, or the [B,H,L] fp32 ln D_t that pisa_attn_fwd_lse wrote
+ *             for this forward call; with NULL the backward recomputes the
+ *             denominators in one more sweep over every row's keys
  *   dout      the gradient of the loss with respect to o
  *   dq, dk, dv receive the gradients, shaped and typed like q, k, v
  *   ws        at least pisa_bwd_workspace_bytes(shape) bytes, 256-aligned:
@@ -196,8 +210,8 @@ pisa_status_t pisa_attn_fwd(const pisa_shape_t *shape, const void *q, const pisa
 size_t pisa_bwd_workspace_bytes(const pisa_shape_t *shape);
 pisa_status_t pisa_attn_bwd(const pisa_shape_t *shape, const void *q, const void *k, const void *v,
                             const pisa_stats_t *st, const int32_t *idx, int32_t topk, double scale,
-                            const void *o, const void *dout, void *dq, void *dk, void *dv, void *ws,
-                            size_t ws_bytes, void *stream);
+                            const void *o, const float *lse, const void *dout, void *dq, void *dk,
+                            void *dv, void *ws, size_t ws_bytes, void *stream);
 
 /* pisa_block_stats followed by pisa_attn_fwd in one call that allocates
  * nothing and takes no workspace, for callers that cannot allocate device

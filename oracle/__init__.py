@@ -234,6 +234,21 @@ def head_forward(q, k, v, *, block: int, topk: int, scale: float, variant: str =
     return o, idx
 
 
+def head_log_denominator(q, k, v, *, block: int, idx: np.ndarray, scale: float) -> np.ndarray:
+    """ln D_t for every row of one (batch, head) under the selection idx: the
+    natural log of the denominator of the gist's "Core Algorithm" N_t / D_t,
+    taken over unshifted exponentials (m_t plus the log of the shifted sum).
+    It is the same for all three variants, whose first-order terms add nothing
+    to D_t. q, k, v: [L, D] float64; returns [L]."""
+    L = q.shape[0]
+    st = block_stats(q, k, v, block)
+    out = np.empty(L)
+    for i in range(st["kbar"].shape[0]):
+        _, Dt, m = pisa_rows(q, k, v, st, idx[i], i, block, scale, False)
+        out[i * block:min(L, (i + 1) * block)] = m + np.log(Dt)
+    return out
+
+
 def head_backward(q, k, v, do, *, block: int, idx: np.ndarray, scale: float):
     """Gradients of the zeroth-order-only forward pass (README, "Kernel
     variants": the ``_0th`` variant is the one that supports training) with

@@ -234,9 +234,26 @@ def grad_floor(q, k, v, do, scale: float, D: int) -> float:
     return 2.0 * gamma(D) * scale * nrm(do) * nrm(v) * max(nrm(k), nrm(q)) + 1e-30
 
 
+def lse_bound(q, k, v, st_ref: dict, scale: float, dtype: str, lse_ref: np.ndarray) -> np.ndarray:
+    """Largest error the forward's ln D_t may carry, per row, for one head's
+    fp64 inputs. The exact logits come from the inputs as read (products exact
+    in fp32 for bf16) with an fp32 sum; a centroid logit uses k̄_j rounded to
+    the I/O dtype, off by up to s Σ_d |q_td||k̄_jd| times its unit roundoff;
+    the weights are summed in fp32, in some tiles after rounding them to the
+    I/O dtype (relative 2^-9 for bf16). ln D_t moves by at most the largest
+    logit error plus the relative error of the sum."""
+    u_io = 2.0 ** -9 if dtype == "bf16" else U32
+    qa = np.abs(q)
+    cent = scale * float(u_io) * (qa @ np.abs(st_ref["kbar"]).T).max(axis=1)
+    exact = scale * gamma(q.shape[1]) * (qa @ np.abs(k).T).max(axis=1)
+    return np.maximum(cent, exact) + u_io + 2 * gamma(q.shape[0] + 64) + 1e-6 * (1.0 + np.abs(lse_ref))
+
+
 def check_backward(w: synth.Workload, heads=None):
     """The backward pass on the GPU (all heads, the oracle's selection, the
-    GPU's own forward output) against the oracle's gradients on `heads`."""
+    GPU's own forward output) against the oracle's gradients on `heads`, both
+    with the forward's ln D_t handed over and with the backward recomputing
+    it; and the forward's ln D_t against the oracle's."""
     t0 = time.time()
     log(f"[{w.name}] backward B={w.B} H={w.H} L={w.L} D={w.D} blk={w.block} d={w.density} "
         f"sink={w.sink_idx} {w.dtype}")
@@ -254,15 +271,27 @@ def check_backward(w: synth.Workload, heads=None):
                                            sink_idx=w.sink_idx, cov_weight=w.cov_weight, cov_ord=w.cov_norm)
     idx_d = torch.from_numpy(idx.astype(np.int32)).to(dev)
     st = bsa.block_stats(qd, kd, vd, w.block)
-    o = bsa.attn_fwd(qd, st, idx_d, w.scale, "0th")
-    dq, dk, dv = bsa.attn_bwd(qd, kd, vd, st, idx_d, w.scale, o, dod)
+    o, lse = bsa.attn_fwd(qd, st, idx_d, w.scale, "0th", return_lse=True)
+    o_plain = bsa.attn_fwd(qd, st, idx_d, w.scale, "0th")
+    dq, dk, dv = bsa.attn_bwd(qd, kd, vd, st, idx_d, w.scale, o, dod, lse=lse)
+    dq2, dk2, dv2 = bsa.attn_bwd(qd, kd, vd, st, idx_d, w.scale, o, dod)
     torch.cuda.synchronize()
+    assert torch.equal(o, o_plain), "the output does not depend on whether ln D_t is written"
     g = [x.float().cpu().numpy() for x in (dq, dk, dv)]
+    g2 = [x.float().cpu().numpy() for x in (dq2, dk2, dv2)]
+    lse_h = lse.cpu().numpy()
     for (b, h) in heads:
         qh, kh, vh, doh = (synth.as_f64(x[b, h]) for x in (q, k, v, do))
+        lref = oracle.head_log_denominator(qh, kh, vh, block=w.block, idx=idx[b, h], scale=w.scale)
+        bound = lse_bound(qh, kh, vh, oracle.block_stats(qh, kh, vh, w.block), w.scale, w.dtype, lref)
+        err = np.abs(lse_h[b, h].astype(np.float64) - lref)
+        log(f"    head ({b},{h}) ln D_t: max-abs {err.max():.3e}, largest fraction of its bound "
+            f"{(err / bound).max():.3f}")
+        assert np.isfinite(lse_h[b, h]).all() and (err <= bound).all(), "ln D_t outside its bound"
         ref = oracle.head_backward(qh, kh, vh, doh, block=w.block, idx=idx[b, h], scale=w.scale)
         fl = grad_floor(qh, kh, vh, doh, w.scale, w.D)
-        for name, gg, rr in zip(("dq", "dk", "dv"), g, ref):
+        for name, gg, gg2, rr in zip(("dq", "dk", "dv"), g, g2, ref):
             compare_grad(gg[b, h], rr, w.dtype, f"head ({b},{h}) {name}", fl)
+            compare_grad(gg2[b, h], rr, w.dtype, f"head ({b},{h}) {name}, denominators recomputed", fl)
     log(f"[{w.name}] backward ok in {time.time() - t0:.1f}s")
-    return dict(st=st, idx=idx_d, o=o, grads=(dq, dk, dv), inputs=(qd, kd, vd, dod))
+    return dict(st=st, idx=idx_d, o=o, lse=lse, grads=(dq, dk, dv), inputs=(qd, kd, vd, dod))

@@ -111,6 +111,15 @@ def test_bad_arguments_rejected():
     assert fwd(q=None) == E and fwd(q=FAKE + 8) == E and fwd(o=None) == E
     assert fwd(fo=3) == E and fwd(fo=-1) == E and fwd(k=0) == E and fwd(k=17) == E and fwd(idx=None) == E
     assert fwd(scale=-1.0) == E
+    fwd_lse = lambda lse=FAKE, q=FAKE, k=2: lib.pisa_attn_fwd_lse(ctypes.byref(s), q, ctypes.byref(st), 0, FAKE,
+                                                                k, 0.1, FAKE, lse, None)
+    assert fwd_lse(lse=None) == E and fwd_lse(lse=FAKE + 2) == E  # ln D_t output missing or misaligned
+    assert fwd_lse(q=None) == E and fwd_lse(k=0) == E
+    bwd = lambda lse=None, ws=FAKE, nws=1 << 40, k=2, kk=FAKE: lib.pisa_attn_bwd(
+        ctypes.byref(s), FAKE, kk, FAKE, ctypes.byref(st), FAKE, k, 0.1, FAKE, lse, FAKE, FAKE, FAKE, FAKE,
+        ws, nws, None)
+    assert bwd(lse=FAKE + 2) == E  # misaligned ln D_t
+    assert bwd(kk=None) == E and bwd(k=0) == E and bwd(ws=FAKE + 16) == E and bwd(nws=10) == E
     assert lib.pisa_block_stats(ctypes.byref(s), FAKE, None, FAKE, ctypes.byref(st), None) == E
     assert lib.pisa_block_stats(ctypes.byref(s), FAKE, FAKE, FAKE, None, None) == E
     assert lib.dense_attn_fwd(ctypes.byref(s), FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, 10, None) == E

@@ -13,7 +13,7 @@ import block_sparse_attention_stats_amd as bsa
 
 pytestmark = pytest.mark.skipif(not os.path.exists(bsa.LIB_PATH), reason="libpisa.so not built")
 
-HOST_ONLY = {"pisa_workspace_bytes", "dense_workspace_bytes", "pisa_status_string"}
+HOST_ONLY = {"pisa_workspace_bytes", "dense_workspace_bytes", "pisa_bwd_workspace_bytes", "pisa_status_string"}
 
 
 class _Guard:
@@ -128,3 +128,16 @@ def test_dense_checks():
     raises("out has shape", bsa.dense, q, q, q, out=q_bf16(L_=10))
     raises("ws must be", bsa.dense, q, q, q, ws=torch.zeros(10, dtype=torch.int32))
     raises("on the GPU", bsa.dense, q, q, q)
+
+
+def test_backward_checks():
+    st = cpu_stats()
+    q = q_bf16()
+    lse_ok = torch.zeros(B, H, L, dtype=torch.float32)
+    raises("o has shape", bsa.attn_bwd, q, q, q, st, idx_ok(), 0.1, q_bf16(L_=999), q)
+    raises("dout has dtype", bsa.attn_bwd, q, q, q, st, idx_ok(), 0.1, q, torch.zeros(B, H, L, D))
+    raises("idx has shape", bsa.attn_bwd, q, q, q, st, idx_ok(n=N + 1), 0.1, q, q)
+    raises("lse has shape", bsa.attn_bwd, q, q, q, st, idx_ok(), 0.1, q, q, lse=torch.zeros(B, H, L + 1))
+    raises("lse has dtype", bsa.attn_bwd, q, q, q, st, idx_ok(), 0.1, q, q,
+           lse=torch.zeros(B, H, L, dtype=torch.float64))
+    raises("on the GPU", bsa.attn_bwd, q, q, q, st, idx_ok(), 0.1, q, q, lse=lse_ok)

@@ -66,13 +66,14 @@ def test_backward_deterministic_and_blhd():
     w = W("bwd_layout", 1, 3, 1500, 128, 64, 0.2, "bf16", "0th", 0, 0.0, seed=421)
     res = check_backward(w, heads=[(0, 1)])
     qd, kd, vd, dod = res["inputs"]
-    st, idx, o = res["st"], res["idx"], res["o"]
-    again = bsa.attn_bwd(qd, kd, vd, st, idx, w.scale, o, dod)
+    st, idx, o, lse = res["st"], res["idx"], res["o"], res["lse"]
+    again = bsa.attn_bwd(qd, kd, vd, st, idx, w.scale, o, dod, lse=lse)
     tr = lambda x: x.transpose(1, 2).contiguous()
     st_t = bsa.block_stats(tr(qd), tr(kd), tr(vd), w.block, layout="BLHD")
-    o_t = bsa.attn_fwd(tr(qd), st_t, idx, w.scale, "0th")
-    g_t = bsa.attn_bwd(tr(qd), tr(kd), tr(vd), st_t, idx, w.scale, o_t, tr(dod))
+    o_t, lse_t = bsa.attn_fwd(tr(qd), st_t, idx, w.scale, "0th", return_lse=True)
+    g_t = bsa.attn_bwd(tr(qd), tr(kd), tr(vd), st_t, idx, w.scale, o_t, tr(dod), lse=lse_t)
     torch.cuda.synchronize()
+    assert torch.equal(lse, lse_t)  # [B,H,L] in either layout
     for a, b, c in zip(res["grads"], again, g_t):
         assert torch.equal(a, b)
         assert torch.equal(tr(a), c)
@@ -80,8 +81,9 @@ def test_backward_deterministic_and_blhd():
 
 def test_autograd_through_zeroth_order_variant():
     """piecewise_sparse_attention_0th on tensors that require gradients records
-    pisa_attn_bwd as its backward: loss.backward() gives the gradients of the
-    direct call bit for bit, and they match the oracle's."""
+    pisa_attn_bwd as its backward, fed the forward's ln D_t: loss.backward()
+    gives the gradients of the direct calls bit for bit, and they match the
+    oracle's."""
     w = W("bwd_autograd", 1, 2, 1000, 128, 64, 0.2, "bf16", "0th", -1, 0.0, seed=431)
     q, k, v = synth.make_qkv(w)
     do = synth.grad_out(w)
@@ -93,8 +95,9 @@ def test_autograd_through_zeroth_order_variant():
     torch.cuda.synchronize()
     with torch.no_grad():
         st = bsa.block_stats(qd.detach(), kd.detach(), vd.detach(), w.block)
+        _, lse = bsa.attn_fwd(qd.detach(), st, idx, w.scale, "0th", return_lse=True)
         direct = bsa.attn_bwd(qd.detach(), kd.detach(), vd.detach(), st, idx, w.scale, o.detach(),
-                              do.to(dev))
+                              do.to(dev), lse=lse)
     torch.cuda.synchronize()
     for x, g in zip((qd, kd, vd), direct):
         assert torch.equal(x.grad, g)

@@ -2,7 +2,12 @@
 "Kernel variants": the ``_0th`` form supports training), each against
 something other than the backward's own formulas: central finite differences of
 the oracle's forward, torch autograd of dense attention, closed forms and exact
-invariants of the forward."""
+invariants of the forward. Also the log-denominators ln D_t that a forward
+pass hands to the backward."""
+
+import json
+import math
+import os
 
 import numpy as np
 import pytest
@@ -120,3 +125,38 @@ def test_invariants_of_the_forward():
     g12 = oracle.head_backward(q, k, v, do + 2.0 * do2, block=block, idx=idx, scale=0.4)
     for a, b, c in zip((dq, dk, dv), g2, g12):
         np.testing.assert_allclose(c, a + 2.0 * b, rtol=0, atol=1e-12)
+
+
+# ------------------------------------------------------------ ln D_t
+def test_log_denominator_worked_example():
+    """The two-block worked example (tests/golden, D_t written by hand term
+    by term, unshifted): ln D_t = ln of the sum of its terms."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "worked_example_2block.json")
+    g = json.load(open(path))
+    q, k, v = (np.array(g["inputs"][x], dtype=np.float64) for x in "qkv")
+    lse = oracle.head_log_denominator(q, k, v, block=2, idx=np.array(g["idx"]), scale=1.0)
+    want = [math.log(sum(a / b * math.exp(c / d) for a, b, c, d in row["D"])) for row in g["rows"]]
+    np.testing.assert_allclose(lse, want, rtol=0, atol=1e-14)
+
+
+def test_log_denominator_dense_and_constant_keys():
+    """Every block selected: ln D_t is the log-sum-exp of the row's logits
+    (torch.logsumexp in fp64). Constant key blocks: the same for any
+    selection, since n_j e^{s q·k̄_j} then equals the block's exact sum. One
+    token: s q·k."""
+    L, D, block = 70, 6, 16
+    q, k, _, _ = rand_inputs(L, D, 21)
+    v = np.zeros_like(q)
+    n = oracle.num_blocks(L, block)
+    dense = torch.logsumexp(0.6 * (torch.from_numpy(q) @ torch.from_numpy(k).T), dim=1).numpy()
+    full = np.tile(np.arange(n), (n, 1))
+    np.testing.assert_allclose(oracle.head_log_denominator(q, k, v, block=block, idx=full, scale=0.6), dense,
+                               rtol=0, atol=1e-12)
+    kc = np.repeat(np.random.default_rng(22).normal(size=(n, D)), block, axis=0)[:L]
+    dense_c = torch.logsumexp(0.6 * (torch.from_numpy(q) @ torch.from_numpy(kc).T), dim=1).numpy()
+    for topk in (1, 3):
+        idx = rand_idx(n, topk, seed=topk + 30)
+        np.testing.assert_allclose(oracle.head_log_denominator(q, kc, v, block=block, idx=idx, scale=0.6),
+                                   dense_c, rtol=0, atol=1e-12)
+    one = oracle.head_log_denominator(q[:1], k[:1], v[:1], block=64, idx=np.array([[0]]), scale=0.6)
+    np.testing.assert_allclose(one, [0.6 * float(q[0] @ k[0])], rtol=0, atol=1e-14)
