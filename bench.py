@@ -114,6 +114,28 @@ def copy_bandwidth(dev, nbytes: int = 2 << 30) -> float:
     return gbs
 
 
+def gemm_rate(dev, dtype_name: str, n: int = 8192) -> float:
+    """TFLOP/s of one plain n x n x n matrix product on the device's GEMM
+    library (hipBLASLt through torch.mm), contiguous operands: what the
+    matrix cores reach on this machine under its power limit, next to the spec
+    peak."""
+    import torch
+    dt = torch.bfloat16 if dtype_name == "bf16" else torch.float32
+    a = torch.randn(n, n, device=dev, dtype=torch.float32).to(dt)
+    b = torch.randn(n, n, device=dev, dtype=torch.float32).to(dt)
+    c = torch.mm(a, b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        torch.mm(a, b, out=c)
+    e1.record()
+    torch.cuda.synchronize()
+    tf = 2.0 * n ** 3 * 5 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del a, b, c
+    return tf
+
+
 def cpu_baseline(w, budget_s: float = 15.0) -> dict:
     """The fp64 oracle, whole heads at a time (statistics, routing and every
     query block of the head), until the time budget is spent; at least one
@@ -316,6 +338,7 @@ def main():
     esz = 2 if w.dtype == "bf16" else 4
     sbytes = stats_bytes(w.B, w.H, w.L, w.D, w.block, esz)
     copy_gbs = copy_bandwidth(dev)
+    gemm_tflops = gemm_rate(dev, w.dtype)
     print(f"[bench] step {ms_step:.3f} ms: stats {ms['block_stats']:.3f} select {ms['select']:.3f} "
           f"fused {ms['attn_fwd']:.3f}; fused {fused_tflops:.1f} TFLOP/s", file=sys.stderr, flush=True)
 
@@ -446,6 +469,7 @@ def main():
         "stats_bytes": sbytes,
         "stats_all_bytes_gbs": sum(sbytes.values()) / (ms["block_stats"] * 1e-3) / 1e9,
         "hbm_copy_gbs": copy_gbs,  # measured device copy, next to the 8 TB/s spec peak
+        "gemm_tflops": gemm_tflops,  # measured library GEMM in the I/O dtype, next to the MFMA spec peak
         "roofline": {"kernel": "k_pisa_fwd", "bound": "mfma", "achieved": fused_tflops, "peak": peak,
                      "unit": "TFLOP/s", "frac": fused_tflops / peak,
                      "traffic": fused_traffic(w.name), "traffic_unit": "bytes per launch"},
