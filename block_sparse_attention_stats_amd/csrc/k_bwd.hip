@@ -65,15 +65,34 @@ __device__ __forceinline__ uint4 op_row(const uint8_t* tile, int rh, int c, int 
 
 // B operand for a contraction over the rows of the 32-row half rh (in vkey
 // order, matching an accumulator used as the A operand), column d = 32 dt + l%32.
+// For 16-bit elements the eight rows of a lane are rows r0..r0+3 and
+// r0+8..r0+11 (r0 = 32 rh + 16 c + 4 h), read with two transposing LDS loads:
+// in each group of 16 lanes, lane j points at 4 elements of row r0 + j/4
+// starting at column 32 dt + 16 (group & 1) + 4 (j % 4), and every lane of the
+// group receives its own column from the four rows.
+typedef short bwd_v4s __attribute__((ext_vector_type(4)));
 template <typename T, int D>
 __device__ __forceinline__ uint4 op_col(const uint8_t* tile, int rh, int dt, int c, int lane) {
   using B = BT<T, D>;
-  const int d = 32 * dt + (lane & 31), h = lane >> 5;
-  T vals[B::KW];
+  const int h = lane >> 5;
+  if constexpr (B::ESZ == 2) {
+    const int g = lane >> 4, j = lane & 15;
+    const int row = 32 * rh + 16 * c + 4 * h + (j >> 2);
+    const int col = 32 * dt + 16 * (g & 1) + 4 * (j & 3);
+    const uint8_t* p = tile + row * B::RP + col * 2;
+    typedef __attribute__((address_space(3))) bwd_v4s* lds_v4s;
+    const bwd_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)p);
+    const bwd_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 8 * B::RP));
+    const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+    return make_uint4(a.x, a.y, b.x, b.y);
+  } else {
+    const int d = 32 * dt + (lane & 31);
+    T vals[B::KW];
 #pragma unroll
-  for (int e = 0; e < B::KW; ++e)
-    vals[e] = *(const T*)(tile + (32 * rh + vkey(B::KW * c + e, h)) * B::RP + d * B::ESZ);
-  return __builtin_bit_cast(uint4, vals);
+    for (int e = 0; e < B::KW; ++e)
+      vals[e] = *(const T*)(tile + (32 * rh + vkey(B::KW * c + e, h)) * B::RP + d * B::ESZ);
+    return __builtin_bit_cast(uint4, vals);
+  }
 }
 
 // Byte offset of token row `row` of head bh in a q, k, v, o or gradient tensor.
