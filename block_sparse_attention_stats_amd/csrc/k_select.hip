@@ -6,6 +6,9 @@
 //   key block) tiles (n x n x D per head: small next to the fused pass); the
 //   sink column gets +infinity. k_scores_mfma (n >= 512) on the fp64 matrix
 //   cores; k_scores (shorter rows) a register-tiled fp64 GEMM through LDS.
+// Rows of up to kRouteMaxBlocks blocks take k_route, which keeps the scores on
+// chip (see there); longer rows take k_scores / k_scores_mfma, whose scores
+// pass through the workspace, and then k_topk.
 // Top-k of a row: the k-th largest key T is narrowed down by an MSB-first
 //   radix select over order-preserving 64-bit keys, stopping early once the
 //   bucket that holds it is to be taken whole; then every key above T and the
@@ -394,6 +397,256 @@ __global__ __launch_bounds__(256) void k_topk_wave(TopkArgs a, long rows) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// k_route: the scores of 16 query blocks and their top-k in one pass, for rows
+// of up to kRouteMaxBlocks blocks; the score matrix never leaves the chip.
+//
+// Phase 1: the workgroup's eight wavefronts share out the key blocks in units
+// of 32 and form q̄_i·k̄_j for the 16 rows on the fp64 matrix cores, in the
+// same products and order as k_scores_mfma. Of each score's order-preserving
+// 64-bit key only the upper 32 bits are kept, in LDS: 16 rows of up to 1280
+// keys is 80 KB, so two workgroups share a CU and each SIMD runs four
+// wavefronts (the fp64 matrix cores reach about 35 TFLOP/s with one wavefront
+// per SIMD and 46-48 with two to four; measured on MI355X).
+// Phase 2: one wavefront per row selects on those 32 bits by a binary radix
+// select that counts with ballots (no LDS traffic). Where the k-th place falls
+// inside a run of keys whose upper halves are equal and only part of the run
+// is taken (a near or exact tie), the wavefront forms the run's scores again,
+// bit for bit as before, and selects within the run on the lower 32 bits; keys
+// equal in all 64 bits go to the lower index, as everywhere else.
+
+constexpr int kRouteRows = 16;
+
+// The raw products of TU tiles of 16 key blocks from col0: acc[u][r] is
+// q̄_i·k̄_j for row i = i0 + g + 4r and key block j = col0 + 16u + c
+// (lane = 16g + c), as 16 x 16 products of v_mfma_f64_16x16x4f64 over d in
+// chunks of 16 (k = g stands for d = d0 + 4g + t in step t). A holds the 16
+// rows' q̄ in that form; columns past the end repeat the last key block
+// (formed, never stored). Each product is the same chain of MFMAs whatever TU
+// and col0, so a product formed again has the same bits.
+template <int D, int TU = 4>
+__device__ __forceinline__ void route_dots(const f64x4 (&A)[D / 16], const double* kb, int col0, int n,
+                                           int g, int c, f64x4 (&acc)[TU]) {
+  const double* pb[TU];
+  f64x4 B[TU];
+#pragma unroll
+  for (int u = 0; u < TU; ++u) {
+    pb[u] = kb + (size_t)min(col0 + 16 * u + c, n - 1) * D + 4 * g;
+    acc[u] = f64x4{0.0, 0.0, 0.0, 0.0};
+    B[u] = *reinterpret_cast<const f64x4*>(pb[u]);
+  }
+#pragma unroll
+  for (int ch = 0; ch < D / 16; ++ch) {
+    f64x4 Bn[TU];
+    if (ch + 1 < D / 16) {
+#pragma unroll
+      for (int u = 0; u < TU; ++u) Bn[u] = *reinterpret_cast<const f64x4*>(pb[u] + 16 * (ch + 1));
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int u = 0; u < TU; ++u)
+        acc[u] = __builtin_amdgcn_mfma_f64_16x16x4f64(A[ch][t], B[u][t], acc[u], 0, 0, 0);
+    if (ch + 1 < D / 16) {
+#pragma unroll
+      for (int u = 0; u < TU; ++u) B[u] = Bn[u];
+    }
+  }
+}
+
+// Routing key of the raw product x for key block j: the score
+// scale·x + cov_weight·M_j (+inf for the sink), mapped by order_key.
+__device__ __forceinline__ unsigned long long route_key(const RouteArgs& a, long bh, double x, int j) {
+  double sc = a.scale * x;
+  if (a.cov_weight != 0.0) sc = sc + a.cov_weight * a.mnorm[bh * a.n + j];
+  if (j == a.sink_block) sc = __builtin_huge_val();
+  return order_key(sc);
+}
+
+// Wave-wide OR / AND of a 32-bit value through DPP (within rows of 16 lanes)
+// and the four rows' first lanes; the result is uniform.
+__device__ __forceinline__ uint32_t row16_or(uint32_t x) {
+  x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+  x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  x |= (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 0x140, 0xF, 0xF, false);  // row_mirror
+  return x;
+}
+__device__ __forceinline__ uint32_t wave_or32(uint32_t x) {
+  x = row16_or(x);
+  return (uint32_t)(__builtin_amdgcn_readlane((int)x, 0) | __builtin_amdgcn_readlane((int)x, 16) |
+                    __builtin_amdgcn_readlane((int)x, 32) | __builtin_amdgcn_readlane((int)x, 48));
+}
+__device__ __forceinline__ uint32_t wave_and32(uint32_t x) { return ~wave_or32(~x); }
+
+// MSB-first binary radix select over one wavefront's 32-bit keys (key[s] in
+// lane j % 64, slot j / 64), counting with ballots. cand (bit s: slot s of
+// this lane) holds the candidates, ncand of them, of which the kk largest are
+// wanted. Each bit in which the candidates differ splits them: if at least kk
+// have it set, the rest drop out; otherwise all that have it are taken (sel)
+// and the search goes on among the others. On return either ncand == kk (every
+// candidate left is taken) or the candidates left are equal in all 32 bits.
+template <int KPL>
+__device__ __forceinline__ void ballot_select(const uint32_t (&key)[KPL], uint32_t& cand, uint32_t& sel,
+                                              int& kk, int& ncand) {
+  uint32_t vor = 0u, vand = ~0u;
+#pragma unroll
+  for (int s = 0; s < KPL; ++s)
+    if ((cand >> s) & 1u) {
+      vor |= key[s];
+      vand &= key[s];
+    }
+  uint32_t diff = wave_or32(vor) & ~wave_and32(vand);
+  while (diff != 0u && ncand > kk) {
+    const int b = 31 - __clz(diff);
+    diff &= ~(1u << b);
+    uint32_t ones = 0u;
+    int cnt1 = 0;
+#pragma unroll
+    for (int s = 0; s < KPL; ++s) {
+      const uint32_t t = (key[s] >> b) & 1u;
+      ones |= t << s;
+      cnt1 += __popcll(__ballot((t & (cand >> s)) != 0u));
+    }
+    ones &= cand;
+    if (cnt1 >= kk) {
+      cand = ones;
+      ncand = cnt1;
+    } else {
+      sel |= ones;
+      cand &= ~ones;
+      kk -= cnt1;
+      ncand -= cnt1;
+    }
+  }
+}
+
+// Phase 2 for query block i (row il of the workgroup): selection and output.
+// hrow: the row's upper key halves in LDS (this wavefront's alone from now on).
+template <int D, int KPL>
+__device__ __forceinline__ void route_row(const RouteArgs& a, long bh, int i, int il, uint32_t* hrow,
+                                          const double* qb, const double* kb, int i0, int lane) {
+  const int n = a.n, k = a.topk;
+  int32_t* out = a.idx + ((size_t)bh * n + i) * k;
+  uint32_t key[KPL];
+  uint32_t cand = 0u, sel = 0u;
+#pragma unroll
+  for (int s = 0; s < KPL; ++s) {
+    const int j = 64 * s + lane;
+    key[s] = j < n ? hrow[j] : 0u;
+    cand |= (j < n ? 1u : 0u) << s;
+  }
+  int kk = k, ncand = n;
+  ballot_select<KPL>(key, cand, sel, kk, ncand);
+  if (ncand > kk) {
+    // The k-th place falls inside a run of keys equal in their upper halves,
+    // and only part of the run is taken: the run's lower halves, from products
+    // formed again (same code, same bits), decide within it.
+    const int g = lane >> 4, c = lane & 15, g0 = il & 3, r0 = il >> 2;
+    f64x4 A[D / 16];
+    const double* pa = qb + (size_t)min(i0 + c, n - 1) * D + 4 * g;
+#pragma unroll
+    for (int ch = 0; ch < D / 16; ++ch) A[ch] = *reinterpret_cast<const f64x4*>(pa + 16 * ch);
+    uint32_t smask = 0u;  // slots holding part of the run (uniform)
+#pragma unroll
+    for (int s = 0; s < KPL; ++s)
+      if (__ballot((cand >> s) & 1u) != 0ull) smask |= 1u << s;
+    while (smask != 0u) {
+      const int s = __builtin_ctz(smask);
+      smask &= smask - 1u;
+      f64x4 acc[4];
+      route_dots<D>(A, kb, 64 * s, n, g, c, acc);
+      double x = 0.0;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const double v = r0 == 0 ? acc[u][0] : r0 == 1 ? acc[u][1] : r0 == 2 ? acc[u][2] : acc[u][3];
+        const double y = __shfl(v, 16 * g0 + c);  // row il, key block 64s + 16u + (lane & 15)
+        if ((lane >> 4) == u) x = y;
+      }
+      const int j = 64 * s + lane;
+      if (j < n) hrow[j] = (uint32_t)route_key(a, bh, x, j);
+    }
+#pragma unroll
+    for (int s = 0; s < KPL; ++s) key[s] = ((cand >> s) & 1u) ? hrow[64 * s + lane] : 0u;
+    ballot_select<KPL>(key, cand, sel, kk, ncand);
+  }
+  // the taken keys and, of the candidates left (equal in all 64 bits, or all
+  // taken), the kk lowest-index ones, ascending
+  const unsigned long long lt = (1ull << lane) - 1ull;
+  int eq_seen = 0, pos = 0;
+#pragma unroll
+  for (int s = 0; s < KPL; ++s) {
+    const bool above = (sel >> s) & 1u, eq = (cand >> s) & 1u;
+    const unsigned long long beq = __ballot(eq);
+    const bool take = above || (eq && eq_seen + __popcll(beq & lt) < kk);
+    const unsigned long long bt = __ballot(take);
+    const int at = pos + __popcll(bt & lt);
+    if (take && at < k) out[at] = 64 * s + lane;  // exactly k are taken; the bound only guards the row
+    pos += __popcll(bt);
+    eq_seen += __popcll(beq);
+  }
+}
+
+// Phase 1 for the 16 query blocks from i0 of head bh: NW wavefronts (this one
+// is number w) share out the units of 32 key blocks; the upper key halves go
+// to hk, rows of `stride`.
+template <int D, int NW>
+__device__ __forceinline__ void route_scores(const RouteArgs& a, long bh, int i0, int w, int lane,
+                                             uint32_t* hk, int stride) {
+  const int n = a.n, g = lane >> 4, c = lane & 15;
+  const double* qb = a.qbar + (size_t)bh * n * D;
+  const double* kb = a.kbar + (size_t)bh * n * D;
+  // rows past the end repeat the last query block (formed, never selected)
+  f64x4 A[D / 16];
+  const double* pa = qb + (size_t)min(i0 + c, n - 1) * D + 4 * g;
+#pragma unroll
+  for (int ch = 0; ch < D / 16; ++ch) A[ch] = *reinterpret_cast<const f64x4*>(pa + 16 * ch);
+  const int nunit = (n + 31) >> 5;
+  for (int un = w; un < nunit; un += NW) {
+    f64x4 acc[2];
+    route_dots<D, 2>(A, kb, 32 * un, n, g, c, acc);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      const int j = 32 * un + 16 * u + c;
+      if (j < n) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          hk[(g + 4 * r) * stride + j] = (uint32_t)(route_key(a, bh, acc[u][r], j) >> 32);
+      }
+    }
+  }
+}
+
+// One workgroup of NW wavefronts per tile of 16 query blocks; rows of up to
+// 64·KPL blocks, LDS rows of CAP keys; NW / 4 wavefronts per SIMD and two
+// workgroups per CU.
+template <int D, int NW, int KPL, int CAP>
+__global__ __launch_bounds__(64 * NW, NW / 2) void k_route(RouteArgs a) {
+  __shared__ uint32_t hk[kRouteRows * CAP];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  // Workgroups reach the eight XCDs in turn; each XCD takes consecutive row
+  // tiles, so its L2 holds the k̄ of one or two heads at a time.
+  long b = blockIdx.x;
+  if ((a.total & 7) == 0) b = (b & 7) * (a.total >> 3) + (b >> 3);
+  const long bh = b / a.nrt;
+  const int i0 = (int)(b % a.nrt) * kRouteRows;
+  const int n = a.n, k = a.topk;
+  if (k >= n) {
+    for (int il = wv; il < kRouteRows && i0 + il < n; il += NW) {
+      int32_t* out = a.idx + ((size_t)bh * n + i0 + il) * k;
+      for (int j = lane; j < n; j += 64) out[j] = j;
+    }
+    return;
+  }
+  const int stride = (n + 15) & ~15;
+  route_scores<D, NW>(a, bh, i0, wv, lane, hk, stride);
+  __syncthreads();
+  const double* qb = a.qbar + (size_t)bh * n * D;
+  const double* kb = a.kbar + (size_t)bh * n * D;
+  for (int il = wv; il < kRouteRows && i0 + il < n; il += NW)
+    route_row<D, KPL>(a, bh, i0 + il, il, hk + il * stride, qb, kb, i0, lane);
+}
+
 // MFMA products per wavefront of k_scores_mfma (rows x columns of 16 x 16).
 // 4 x 4 needs ~300 registers (one wavefront per SIMD) and still beats 4 x 2
 // and 2 x 2, which fit two and four: fewer operand loads per product count
@@ -435,6 +688,25 @@ hipError_t launch_topk(const TopkArgs& a, long rows, hipStream_t s) {
     default: hipLaunchKernelGGL(k_topk_wave<32>, grid, dim3(256), 0, s, a, rows); break;
   }
   return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_route_d(const RouteArgs& a, hipStream_t s) {
+  const int slots = (a.n + 63) / 64, kpl = (slots + 3) / 4 * 4;
+  const dim3 grid((unsigned)a.total);
+  switch (kpl) {
+    case 4: hipLaunchKernelGGL((k_route<D, 8, 4, 256>), grid, dim3(512), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((k_route<D, 8, 8, 512>), grid, dim3(512), 0, s, a); break;
+    case 12: hipLaunchKernelGGL((k_route<D, 8, 12, 768>), grid, dim3(512), 0, s, a); break;
+    case 16: hipLaunchKernelGGL((k_route<D, 8, 16, 1024>), grid, dim3(512), 0, s, a); break;
+    default: hipLaunchKernelGGL((k_route<D, 8, 20, kRouteMaxBlocks>), grid, dim3(512), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_route(int D, const RouteArgs& a, hipStream_t s) {
+  if (a.n < 1 || a.n > kRouteMaxBlocks) return hipErrorInvalidValue;
+  return D == 64 ? launch_route_d<64>(a, s) : launch_route_d<128>(a, s);
 }
 
 }  // namespace pisa

@@ -18,12 +18,12 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
-// Heads whose routing scores one pass of pisa_select holds: enough for about
-// 2048 workgroups of the score kernel (128 x 128 score tiles from 512 blocks
-// on, 64 x 64 below), at most all of them. The score buffer is sized for one
-// such chunk: about 2048 x 128² fp64 values (256 MiB) at most once n reaches
-// 512 blocks, whatever the head count (one head's n² scores when that alone is
-// more). At the Wan shape two chunks of 20 heads.
+// Rows longer than kRouteMaxBlocks blocks go through a score buffer in the
+// workspace. One pass of pisa_select holds the scores of this many heads:
+// enough for about 2048 workgroups of the score kernel (128 x 128 score
+// tiles), at most all of them. The buffer is sized for one such chunk, about
+// 2048 x 128² fp64 values (256 MiB) whatever the head count (one head's n²
+// scores when that alone is more).
 long route_chunk(long bh, long n) {
   const long t = n >= 512 ? (n + 127) / 128 : (n + 63) / 64;
   const long c = (2048 + t * t - 1) / (t * t);
@@ -77,8 +77,8 @@ pisa_status_t check_shape(const pisa_shape_t* s, pisa::WsLayout* w) {
   off = align256(off + (size_t)bh * s->D * s->D * esz);
   w->hpart = off;
   off = align256(off + (size_t)bh * w->nch * s->D * s->D * sizeof(float));
-  w->scores = off;
-  off = align256(off + (size_t)route_chunk(bh, n) * n * n * sizeof(double));
+  w->scores = off;  // only rows too long for k_route pass their scores through here
+  if (n > pisa::kRouteMaxBlocks) off = align256(off + (size_t)route_chunk(bh, n) * n * n * sizeof(double));
   w->total = off;
   return PISA_OK;
 }
@@ -325,6 +325,21 @@ PISA_API pisa_status_t pisa_select(const pisa_shape_t* shape, const pisa_stats_t
   if ((rc = check_stats(st, w, cov_weight > 0.0)) != PISA_OK) return rc;
   if (idx == nullptr || !aligned(idx, 4)) return PISA_EINVAL;
   hipStream_t s = (hipStream_t)stream;
+  if (w.n <= pisa::kRouteMaxBlocks) {
+    pisa::RouteArgs ra;
+    ra.qbar = st->qbar;
+    ra.kbar = st->kbar;
+    ra.mnorm = st->mnorm;
+    ra.idx = idx;
+    ra.scale = scale;
+    ra.cov_weight = cov_weight;
+    ra.n = w.n;
+    ra.topk = topk;
+    ra.sink_block = sink_idx == PISA_SINK_NONE ? -1 : (sink_idx == 0 ? 0 : w.n - 1);
+    ra.nrt = (w.n + 15) / 16;
+    ra.total = w.bh * ra.nrt;
+    return hip_status(pisa::launch_route(shape->D, ra, s));
+  }
   uint8_t* base = (uint8_t*)st->ws;
   pisa::ScoreArgs sa;
   sa.qbar = st->qbar;

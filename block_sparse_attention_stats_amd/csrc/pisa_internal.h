@@ -13,7 +13,8 @@ struct WsLayout {
   size_t kbp, vbp;    // K-format k̄ / V-format ΣV tiles: [BH][ceil(n/64)][64*D]
   size_t hbt;         // H̄ᵀ operand chunks: [BH][D*D]
   size_t hpart;       // fp32 partial Σ_j H_j per chunk of blocks: [BH][nch][D][D]
-  size_t scores;      // fp64 routing scores: [BH][n][n]
+  size_t scores;      // fp64 routing scores of a chunk of heads: [heads][n][n]; empty when
+                      // n <= kRouteMaxBlocks (k_route keeps them on chip)
   size_t kmax2;       // fp32 largest squared key norm per run of blocks: [BH][nch]
   size_t redo;        // int32 count + list of query tiles the careful kernel recomputes
   size_t sync;        // int32 arrival counter of the fast kernel's generation barrier
@@ -52,6 +53,16 @@ struct TopkArgs {
   const double* scores;
   int32_t* idx;
   int n, topk;
+};
+
+// Scores and top-k in one pass (rows of at most kRouteMaxBlocks blocks).
+struct RouteArgs {
+  const double *qbar, *kbar, *mnorm;
+  int32_t* idx;
+  double scale, cov_weight;
+  int n, topk, sink_block;  // sink_block < 0: none
+  int nrt;                  // workgroups per head: 16 query blocks each
+  long total;               // workgroups in all
 };
 
 struct FwdArgs {
@@ -110,6 +121,8 @@ hipError_t launch_hbar_reduce(int dtype, int D, const StatsArgs& a, long bh, hip
 hipError_t launch_mnorm_spectral(int dtype, int D, const StatsArgs& a, long bh, hipStream_t s);
 hipError_t launch_scores(int D, const ScoreArgs& a, long bh, hipStream_t s);
 hipError_t launch_topk(const TopkArgs& a, long rows, hipStream_t s);
+hipError_t launch_route(int D, const RouteArgs& a, hipStream_t s);
+constexpr int kRouteMaxBlocks = 1280;  // longest row k_route keeps in LDS (80 KB per workgroup)
 // Fast pass, then the careful pass over the query tiles the fast pass queued.
 hipError_t launch_fwd(int dtype, int D, const FwdArgs& a, hipStream_t s);
 
