@@ -331,6 +331,12 @@ __device__ __forceinline__ void xstep(typename Regs<bf16, D>::Acc& oacc,
       py[qt][c] = make_uint4(pw[qt][4 * c], pw[qt][4 * c + 1], pw[qt][4 * c + 2], pw[qt][4 * c + 3]);
 }
 
+// Keys of a wavefront's 32 that lie past the end of the sequence, as a bit
+// mask (bit k: key k), given how many of them are valid.
+__device__ __forceinline__ uint32_t dead_keys(int nvalid) {
+  return nvalid >= 32 ? 0u : (nvalid <= 0 ? ~0u : ~((1u << nvalid) - 1u));
+}
+
 // Careful kernel only: does any row of this sub-tile need a higher running max?
 template <int KIND>
 __device__ __forceinline__ bool tile_max(const f32x16 (&sacc)[2], const float (&m)[2],
@@ -711,11 +717,10 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
         auto cinit = [&](int ct) {
           const int jbase = kSub * ct + 32 * w;
           const int nvalid = a.n - jbase;  // valid centroids from this wavefront's first key
-          uint32_t dead = sh.selmask[jbase >> 5];
-          if (nvalid < 32) dead |= nvalid <= 0 ? ~0u : ~((1u << nvalid) - 1u);
+          const uint32_t dh = (sh.selmask[jbase >> 5] | dead_keys(nvalid)) >> (4 * h);
           f32x16 v;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) v[r] = ((dead >> vkey(r, h)) & 1u) ? kNegInf : 0.0f;
+          for (int r = 0; r < 16; ++r) v[r] = ((dh >> vkey(r, 0)) & 1u) ? kNegInf : 0.0f;
           return v;
         };
         pipelined<T, D, true, false>(
@@ -769,10 +774,11 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
       return (head_sub + (size_t)block_at(t / spb) * spb + (t % spb)) * G::SUB_BYTES;
     };
     auto init = [&](int t) {
-      const int nvalid = t < nt_full ? kSub : a.n_last - kSub * (t - nt_full) - 32 * w;
+      const uint32_t dh =
+          (t < nt_full ? 0u : dead_keys(a.n_last - kSub * (t - nt_full) - 32 * w)) >> (4 * h);
       f32x16 v;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = vkey(r, h) >= nvalid ? kNegInf : 0.0f;
+      for (int r = 0; r < 16; ++r) v[r] = ((dh >> vkey(r, 0)) & 1u) ? kNegInf : 0.0f;
       return v;
     };
     pipelined<T, D, true, true>(
@@ -874,7 +880,7 @@ __device__ __forceinline__ void weights_linear(const f32x16 (&sacc)[2], const fl
       float p[G::KW];
 #pragma unroll
       for (int e = 0; e < G::KW; ++e) {
-        const float sv = sacc[qt][G::KW * c + e];
+        const float sv = acc_read(sacc[qt][G::KW * c + e]);  // one at a time: few live VGPRs
         const float x = fmaf(sv, a1[qt], b1[qt]);
         p[e] = (RAGGED && sv == kNegInf) ? 0.0f : x;
       }
@@ -1049,9 +1055,9 @@ __device__ __forceinline__ void pb1_tile(const FwdArgs& a, long item, FwdShared<
   auto init_g = [&](int g) {
     f32x16 v = f32x16{};
     if (ragged && g >= g_last) {
-      const int nvalid = a.n_last - kSub * (g - g_last) - 32 * w;
+      const uint32_t dh = dead_keys(a.n_last - kSub * (g - g_last) - 32 * w) >> (4 * h);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = vkey(r, h) >= nvalid ? kNegInf : 0.0f;
+      for (int r = 0; r < 16; ++r) v[r] = ((dh >> vkey(r, 0)) & 1u) ? kNegInf : 0.0f;
     }
     return v;
   };
@@ -1121,10 +1127,11 @@ __device__ __forceinline__ void pb1_tile(const FwdArgs& a, long item, FwdShared<
       return (head_sub + (size_t)block_at(t / spb) * spb + (t % spb)) * G::SUB_BYTES;
     };
     auto init = [&](int t) {
-      const int nvalid = t < nt_full ? kSub : a.n_last - kSub * (t - nt_full) - 32 * w;
+      const uint32_t dh =
+          (t < nt_full ? 0u : dead_keys(a.n_last - kSub * (t - nt_full) - 32 * w)) >> (4 * h);
       f32x16 v;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = vkey(r, h) >= nvalid ? kNegInf : 0.0f;
+      for (int r = 0; r < 16; ++r) v[r] = ((dh >> vkey(r, 0)) & 1u) ? kNegInf : 0.0f;
       return v;
     };
     pipelined<T, D, true, true>(nt, a.kp, a.vp, off, [](int) { return f32x16{}; }, init, l, m, cs, qr,
@@ -1137,10 +1144,12 @@ __device__ __forceinline__ void pb1_tile(const FwdArgs& a, long item, FwdShared<
       f32x16 sx[2];
       load_k<T, D>(a.kbp + (head_ct + ct) * G::SUB_BYTES, w, lane, kc);
       mma_s<T, D>(qr, kc, sx);
+      // one base address per lane, the rest constant offsets
+      float* clb = &cl[32 * w + 4 * h][l32];
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) cl[32 * w + vkey(r, h)][32 * qt + l32] = sx[qt][r];
+        for (int r = 0; r < 16; ++r) clb[(vkey(r, 0)) * kSub + 32 * qt] = sx[qt][r];
     }
     // the group's unselected blocks, ascending (both wavefronts count them;
     // wavefront 0 writes the list)
