@@ -223,6 +223,46 @@ def test_routing_exact_scores_and_ties(n):
     log(f"routing n={n}: exact over {len(rows)} query blocks x {H} heads, k in {ks}")
 
 
+@pytest.mark.parametrize("n", [64, 300, 1182, 1280, 1500])
+def test_routing_ties_in_the_upper_key_bits(n):
+    """Scores that agree in the upper 32 bits of their order keys and differ
+    only below, or not at all, right at the k-th place. q̄_i is the unit vector
+    e_(i mod D) and the scale 1/8, so S_ij = k̄_j[i mod D] / 8 exactly in fp64
+    on both sides. Each coordinate of k̄ holds a band of scores well above the
+    cut, a cluster 1 + m·2^-52 (m < 2^31: one exponent and the same upper 20
+    mantissa bits) with some values repeated, and the rest well below; k cuts
+    the cluster, so the selection rests on the lower key bits and, for the
+    repeated values, on the lower index. Stats are filled directly and the
+    selection is compared with the oracle's exactly."""
+    dev = torch.device("cuda:0")
+    D, H = 64, 2
+    rng = np.random.default_rng(4000 + n)
+    shape = bsa.make_shape(torch.empty((1, H, n * 64, D), dtype=torch.bfloat16, device=dev), 64)
+    st = bsa.alloc_stats(shape, dev, want_mnorm=False)
+    qbar = np.zeros((1, H, n, D))
+    for i in range(n):
+        qbar[0, :, i, i % D] = 1.0
+    n_above, n_cluster = n // 8, max(8, n // 4)
+    kbar = np.empty((1, H, n, D))
+    for h in range(H):
+        for d in range(D):
+            m = rng.integers(0, 1 << 31, size=n_cluster)
+            m[: n_cluster // 4] = m[n_cluster // 4: 2 * (n_cluster // 4)]  # exact repeats
+            col = np.concatenate([2.0 + rng.random(n_above), 1.0 + m * 2.0 ** -52,
+                                  0.5 * rng.random(n - n_above - n_cluster)])
+            kbar[0, h, :, d] = col[rng.permutation(n)]
+    st.qbar.copy_(torch.from_numpy(qbar))
+    st.kbar.copy_(torch.from_numpy(kbar))
+    scale = 0.125
+    for topk in (n_above + n_cluster // 2, n_above + n_cluster // 2 + 1):
+        idx = bsa.select(st, topk, scale).cpu().numpy()
+        for h in range(H):
+            ref = oracle.select_topk(oracle.pooled_scores(qbar[0, h], kbar[0, h], scale), topk)
+            bad = np.nonzero((idx[0, h] != ref).any(axis=1))[0]
+            assert bad.size == 0, f"n={n} topk={topk} head {h}: {bad.size} rows differ, first {bad[0]}"
+    log(f"routing n={n}: ties in the upper key bits resolved exactly, {H} heads x {n} rows")
+
+
 JOINT_CASES = [
     # (workload, first-part length L0, layout): text first on a block boundary
     # (FLUX's 512 text tokens), image first with the boundary inside a block
