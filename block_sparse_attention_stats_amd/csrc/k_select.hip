@@ -4,16 +4,16 @@
 //
 // Scores: S_ij = scale * q̄_i·k̄_j + cov_weight * M_j in fp64 over (query block,
 //   key block) tiles (n x n x D per head: small next to the fused pass); the
-//   sink column gets +infinity. k_scores_mfma (n >= 512) on the fp64 matrix
-//   cores; k_scores (shorter rows) a register-tiled fp64 GEMM through LDS.
+//   sink column gets +infinity. Both paths form them with the same products
+//   on the fp64 matrix cores.
 // Rows of up to kRouteMaxBlocks blocks take k_route, which keeps the scores on
-// chip (see there); longer rows take k_scores / k_scores_mfma, whose scores
-// pass through the workspace, and then k_topk.
+// chip (see there); longer rows take k_scores_mfma, whose scores pass through
+// the workspace, and then k_topk_wave or k_topk.
 // Top-k of a row: the k-th largest key T is narrowed down by an MSB-first
 //   radix select over order-preserving 64-bit keys, stopping early once the
 //   bucket that holds it is to be taken whole; then every key above T and the
 //   lowest-index keys equal to it are taken, and the indices emitted ascending.
-//   k_topk_wave (rows of up to 2048 blocks): one wavefront per row, its keys in
+//   k_topk_wave (rows of 1281 to 2048 blocks): one wavefront per row, its keys in
 //   registers; each pass's 8-bit digit starts at the highest bit in which the
 //   remaining candidates still differ, so no pass is spent on the sign and
 //   exponent bits they share. k_topk (longer rows): one workgroup per row, the
@@ -23,80 +23,10 @@
 
 namespace pisa {
 
-// k_scores tile: TM x TM (query block, key block) pairs per workgroup, each of
-// the 256 threads owning an (TM/16) x (TM/16) block of them (TM = 64 for the
-// rows it serves, n < 512).
-template <int D, int TM>
-__global__ __launch_bounds__(256) void k_scores(ScoreArgs a) {
-  // Rows ty + 16x, columns tx + 16y. The dot products run over d in order, one
-  // fp64 FMA per term. The next chunk of q̄ / k̄ is read into registers while
-  // the current one is consumed from LDS.
-  constexpr int KC = 8, R = TM / 16, PER = TM * KC / 256;
-  __shared__ double As[KC][TM + 1], Bs[KC][TM + 1];
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const long bh = blockIdx.z;
-  const int i0 = blockIdx.y * TM, j0 = blockIdx.x * TM;
-  const double* qb = a.qbar + (size_t)bh * a.n * D;
-  const double* kb = a.kbar + (size_t)bh * a.n * D;
-  double acc[R][R];
-#pragma unroll
-  for (int x = 0; x < R; ++x)
-#pragma unroll
-    for (int y = 0; y < R; ++y) acc[x][y] = 0.0;
-  double pa[PER], pb[PER];
-  auto fetch = [&](int d0) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int x = tid + 256 * u, row = x / KC, dd = x % KC;
-      pa[u] = (i0 + row < a.n) ? qb[(size_t)(i0 + row) * D + d0 + dd] : 0.0;
-      pb[u] = (j0 + row < a.n) ? kb[(size_t)(j0 + row) * D + d0 + dd] : 0.0;
-    }
-  };
-  fetch(0);
-  for (int d0 = 0; d0 < D; d0 += KC) {
-#pragma unroll
-    for (int u = 0; u < PER; ++u) {
-      const int x = tid + 256 * u, row = x / KC, dd = x % KC;
-      As[dd][row] = pa[u];
-      Bs[dd][row] = pb[u];
-    }
-    __syncthreads();
-    if (d0 + KC < D) fetch(d0 + KC);
-#pragma unroll
-    for (int dd = 0; dd < KC; ++dd) {
-      double av[R], bv[R];
-#pragma unroll
-      for (int x = 0; x < R; ++x) av[x] = As[dd][ty + 16 * x];
-#pragma unroll
-      for (int y = 0; y < R; ++y) bv[y] = Bs[dd][tx + 16 * y];
-#pragma unroll
-      for (int x = 0; x < R; ++x)
-#pragma unroll
-        for (int y = 0; y < R; ++y) acc[x][y] = fma(av[x], bv[y], acc[x][y]);
-    }
-    __syncthreads();
-  }
-  double* out = a.scores + (size_t)bh * a.n * a.n;
-#pragma unroll
-  for (int y = 0; y < R; ++y) {
-    const int j = j0 + tx + 16 * y;
-    if (j >= a.n) continue;
-    const double cov = a.cov_weight != 0.0 ? a.cov_weight * a.mnorm[bh * a.n + j] : 0.0;
-#pragma unroll
-    for (int x = 0; x < R; ++x) {
-      const int i = i0 + ty + 16 * x;
-      if (i >= a.n) continue;
-      double sc = a.scale * acc[x][y];
-      if (a.cov_weight != 0.0) sc = sc + cov;
-      if (j == a.sink_block) sc = __builtin_huge_val();
-      out[(size_t)i * a.n + j] = sc;
-    }
-  }
-}
-
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 
-// k_scores_mfma: the same scores on the fp64 matrix cores, for n >= 512.
+// k_scores_mfma: the pooled scores on the fp64 matrix cores, for rows longer than
+// kRouteMaxBlocks.
 // Each wavefront computes 16·TR x 16·TC (query block, key block) pairs as
 // TR x TC products of v_mfma_f64_16x16x4f64 (A: row m = lane % 16,
 // k = lane / 16; B: k = lane / 16, column = lane % 16; D: element r of a
@@ -653,19 +583,14 @@ __global__ __launch_bounds__(64 * NW, NW / 2) void k_route(RouteArgs a) {
 // for more than occupancy here.
 constexpr int kScoreTR = 4, kScoreTC = 4;
 
+// Rows longer than kRouteMaxBlocks only (n > 1280).
 hipError_t launch_scores(int D, const ScoreArgs& a, long bh, hipStream_t s) {
-  if (a.n >= 512) {
-    constexpr int TR = kScoreTR, TC = kScoreTC;
-    dim3 grid((unsigned)((a.n + 32 * TC - 1) / (32 * TC)), (unsigned)((a.n + 32 * TR - 1) / (32 * TR)),
-              (unsigned)bh);
-    if (D == 64) hipLaunchKernelGGL((k_scores_mfma<64, TR, TC>), grid, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL((k_scores_mfma<128, TR, TC>), grid, dim3(256), 0, s, a);
-    return hipGetLastError();
-  }
-  const unsigned t = (unsigned)((a.n + 63) / 64);
-  dim3 grid(t, t, (unsigned)bh);
-  if (D == 64) hipLaunchKernelGGL((k_scores<64, 64>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_scores<128, 64>), grid, dim3(256), 0, s, a);
+  if (a.n <= kRouteMaxBlocks) return hipErrorInvalidValue;
+  constexpr int TR = kScoreTR, TC = kScoreTC;
+  dim3 grid((unsigned)((a.n + 32 * TC - 1) / (32 * TC)), (unsigned)((a.n + 32 * TR - 1) / (32 * TR)),
+            (unsigned)bh);
+  if (D == 64) hipLaunchKernelGGL((k_scores_mfma<64, TR, TC>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_scores_mfma<128, TR, TC>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -676,13 +601,10 @@ hipError_t launch_topk(const TopkArgs& a, long rows, hipStream_t s) {
     hipLaunchKernelGGL(k_topk, dim3((unsigned)rows), dim3(256), lds, s, a);
     return hipGetLastError();
   }
+  // rows of 1281 to 2048 blocks: 21 to 32 register slots
+  if (a.n <= kRouteMaxBlocks) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((rows + 3) / 4));
   switch ((slots + 3) / 4) {
-    case 1: hipLaunchKernelGGL(k_topk_wave<4>, grid, dim3(256), 0, s, a, rows); break;
-    case 2: hipLaunchKernelGGL(k_topk_wave<8>, grid, dim3(256), 0, s, a, rows); break;
-    case 3: hipLaunchKernelGGL(k_topk_wave<12>, grid, dim3(256), 0, s, a, rows); break;
-    case 4: hipLaunchKernelGGL(k_topk_wave<16>, grid, dim3(256), 0, s, a, rows); break;
-    case 5: hipLaunchKernelGGL(k_topk_wave<20>, grid, dim3(256), 0, s, a, rows); break;
     case 6: hipLaunchKernelGGL(k_topk_wave<24>, grid, dim3(256), 0, s, a, rows); break;
     case 7: hipLaunchKernelGGL(k_topk_wave<28>, grid, dim3(256), 0, s, a, rows); break;
     default: hipLaunchKernelGGL(k_topk_wave<32>, grid, dim3(256), 0, s, a, rows); break;

@@ -188,9 +188,10 @@ def test_random_wider_shapes(w):
 
 # row lengths (blocks) for routing: the on-chip score-and-select kernel from
 # one to twenty register slots per lane (full and one past full) up to its
-# longest row (1280); past it the score kernel with the wavefront top-k (up to
-# 2048 blocks), the workgroup top-k beyond, and the longest row the library takes
-ROUTE_N = [1, 2, 63, 64, 256, 257, 700, 1182, 1280, 1281, 1861, 2048, 2049, 8192]
+# longest row (1280); past it the score kernel with the wavefront top-k (24, 28
+# and 32 register slots, up to 2048 blocks), the workgroup top-k beyond, and
+# the longest row the library takes
+ROUTE_N = [1, 2, 63, 64, 256, 257, 700, 1182, 1280, 1281, 1600, 1861, 2048, 2049, 8192]
 
 
 @pytest.mark.parametrize("n", ROUTE_N)
