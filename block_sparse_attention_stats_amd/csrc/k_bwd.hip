@@ -381,9 +381,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkv(BwdArgs a) {
   const float cs = a.scale * kLog2e;
   long bh;
   int j = 0, ct = 0, k0 = 0;
+  int i_lo = 0, i_hi = a.n, part = 0;  // the query blocks this workgroup visits lie in [i_lo, i_hi)
   if constexpr (CENT) {
-    bh = blockIdx.x / a.nct;
-    ct = (int)(blockIdx.x % a.nct);
+    part = (int)(blockIdx.x % a.cparts);
+    const long rest = blockIdx.x / a.cparts;
+    bh = rest / a.nct;
+    ct = (int)(rest % a.nct);
+    i_lo = (int)((long)part * a.n / a.cparts);
+    i_hi = (int)((long)(part + 1) * a.n / a.cparts);
   } else {
     const int st = (int)(blockIdx.x % SPB);
     const long rest = blockIdx.x / SPB;
@@ -401,10 +406,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkv(BwdArgs a) {
   auto list_chunk = [&](int from) {
     if (w != 0) return;
     int cnt = 0, ib = from;
-    for (; ib < a.n && cnt <= kQChunk - 64; ib += 64) {
+    for (; ib < i_hi && cnt <= kQChunk - 64; ib += 64) {
       const int i = ib + lane;
       bool take = false;
-      if (i < a.n) {
+      if (i < i_hi) {
         if constexpr (CENT) take = (selected64(a, bh, i, ct) & valid_c) != valid_c;
         else take = selected(a, bh, i, j);
       }
@@ -417,7 +422,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkv(BwdArgs a) {
       qnext = ib;
     }
   };
-  list_chunk(0);
+  list_chunk(i_lo);
   {
     uint4 pk[PER], pv[PER];
     const Rows kr = CENT ? centroid_rows<T, D>(a, a.kbt, bh) : tensor_rows(a, a.k, bh);
@@ -500,7 +505,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkv(BwdArgs a) {
         }
       }
     }
-    if (from >= a.n) break;
+    if (from >= i_hi) break;
     __syncthreads();  // every thread has read qcount, qnext and its last list entry
     list_chunk(from);
     __syncthreads();
@@ -518,7 +523,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkv(BwdArgs a) {
       const int xx = 32 * xh + vkey(r, h), d = 32 * dt + l32;
       if constexpr (CENT) {
         const int jc = 64 * ct + xx;
-        if (jc < a.n) {
+        if (a.cparts > 1) {  // raw partial sums, added up by k_bwd_cent_reduce
+          const size_t pidx = (((size_t)part * (gridDim.x / a.cparts / a.nct) + bh) * a.nct * 64 + jc) * D + d;
+          a.dkbar_p[pidx] = dk[dt][r];
+          a.dvsum_p[pidx] = dv[dt][r];
+        } else if (jc < a.n) {
           a.dkbar[((size_t)bh * a.n + jc) * D + d] = a.scale * dk[dt][r];
           a.dvsum[((size_t)bh * a.n + jc) * D + d] = dv[dt][r];
         }
@@ -534,6 +543,27 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkv(BwdArgs a) {
         }
       }
     }
+}
+
+// The centroid gradients from their partial sums over ranges of query
+// blocks, added in range order (deterministic): dk̄_j = s Σ_p part_p.
+template <int D>
+__global__ void k_bwd_cent_reduce(BwdArgs a, long bh_total) {
+  const size_t per = (size_t)bh_total * a.nct * 64 * D;
+  for (long x = (long)blockIdx.x * 256 + threadIdx.x; x < bh_total * a.n * D; x += (long)gridDim.x * 256) {
+    const long r = x / D;
+    const int d = (int)(x % D);
+    const long bh = r / a.n;
+    const int jc = (int)(r % a.n);
+    const size_t o = ((size_t)bh * a.nct * 64 + jc) * D + d;
+    float sk = 0.0f, sv = 0.0f;
+    for (int p = 0; p < a.cparts; ++p) {
+      sk += a.dkbar_p[p * per + o];
+      sv += a.dvsum_p[p * per + o];
+    }
+    a.dkbar[x] = a.scale * sk;
+    a.dvsum[x] = sv;
+  }
 }
 
 // k̄_j and ΣV_j as rows in the I/O dtype (zero past n), for the centroid tiles.
@@ -574,7 +604,10 @@ hipError_t launch_bwd_t(const BwdArgs& a, long bh, hipStream_t s) {
   hipLaunchKernelGGL((k_bwd_prep<T, D>), dim3((unsigned)min(4096L, (crow * D + 255) / 256)), dim3(256), 0, s, a,
                      crow);
   hipLaunchKernelGGL((k_bwd_dq<T, D, SPB>), dim3((unsigned)(bh * a.n * SPB)), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((k_bwd_dkv<T, D, SPB, true>), dim3((unsigned)(bh * a.nct)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_bwd_dkv<T, D, SPB, true>), dim3((unsigned)(bh * a.nct * a.cparts)), dim3(256), 0, s, a);
+  if (a.cparts > 1)
+    hipLaunchKernelGGL((k_bwd_cent_reduce<D>), dim3((unsigned)min(4096L, (bh * a.n * D + 255) / 256)), dim3(256), 0,
+                       s, a, bh);
   hipLaunchKernelGGL((k_bwd_dkv<T, D, SPB, false>), dim3((unsigned)(bh * a.n * SPB)), dim3(256), 0, s, a);
   return hipGetLastError();
 }

@@ -24,6 +24,18 @@ namespace pisa {
 // SEG: the sequence is held in two tensors (rows from L0 on in q1, k1, v1).
 // Without it the kernel never touches the second part, which keeps its state
 // out of the registers the single-tensor case needs.
+// Two transposed 8-byte LDS reads (gfx950's ds_read_b64_tr_b16) at p and
+// eight rows further: the 16-bit MFMA operand of one column over two runs of
+// four rows.
+typedef short stats_v4s __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 col8_tr(const uint8_t* p, int pitch) {
+  typedef __attribute__((address_space(3))) stats_v4s* lds_v4s;
+  const stats_v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)p);
+  const stats_v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s)(p + 8 * pitch));
+  const uint2 x = __builtin_bit_cast(uint2, lo), y = __builtin_bit_cast(uint2, hi);
+  return make_uint4(x.x, x.y, y.x, y.y);
+}
+
 template <typename T, int D, int MODE, bool SEG>
 __global__ __launch_bounds__(256, 2) void k_block_stats(StatsArgs a) {
   using G = Geo<T, D>;
@@ -235,16 +247,28 @@ __global__ __launch_bounds__(256, 2) void k_block_stats(StatsArgs a) {
           uint4 A[TW], B[TW];
 #pragma unroll
           for (int x = 0; x < TW; ++x) {
-            T av[KW], bv[KW];
-            const int dA = 32 * (dt0 + x) + l32, dB = 32 * (et0 + x) + l32;
+            if constexpr (ESZ == 2) {
+              // the eight key rows of vkey order are two runs of four: one
+              // transposed read each (ds_read_b64_tr_b16; in each group of 16
+              // lanes, lane i points at 4 elements of row r0 + i/4 from column
+              // c0 + 4 (i % 4), and each lane receives its own column c0 + i)
+              const int g = lane >> 4, i = lane & 15;
+              const int row = 32 * w + 16 * c + 4 * h + (i >> 2);
+              const int col = 16 * (g & 1) + 4 * (i & 3);
+              A[x] = col8_tr(&tile[KT][row * PITCH + (32 * (dt0 + x) + col) * 2], PITCH);
+              B[x] = col8_tr(&tile[VT][row * PITCH + (32 * (et0 + x) + col) * 2], PITCH);
+            } else {
+              T av[KW], bv[KW];
+              const int dA = 32 * (dt0 + x) + l32, dB = 32 * (et0 + x) + l32;
 #pragma unroll
-            for (int e = 0; e < KW; ++e) {
-              const int row = (32 * w + vkey(KW * c + e, h)) * PITCH;
-              av[e] = *(const T*)(&tile[KT][row + dA * ESZ]);
-              bv[e] = *(const T*)(&tile[VT][row + dB * ESZ]);
+              for (int e = 0; e < KW; ++e) {
+                const int row = (32 * w + vkey(KW * c + e, h)) * PITCH;
+                av[e] = *(const T*)(&tile[KT][row + dA * ESZ]);
+                bv[e] = *(const T*)(&tile[VT][row + dB * ESZ]);
+              }
+              A[x] = __builtin_bit_cast(uint4, av);
+              B[x] = __builtin_bit_cast(uint4, bv);
             }
-            A[x] = __builtin_bit_cast(uint4, av);
-            B[x] = __builtin_bit_cast(uint4, bv);
           }
 #pragma unroll
           for (int x = 0; x < TW; ++x)

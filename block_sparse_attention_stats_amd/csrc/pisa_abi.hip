@@ -454,6 +454,19 @@ pisa::BwdLayout bwd_layout(const pisa_shape_t* s, const pisa::WsLayout& w) {
   off = align256(off + (size_t)w.bh * w.nct * 64 * s->D * w.esz);
   b.vbt = off;
   off = align256(off + (size_t)w.bh * w.nct * 64 * s->D * w.esz);
+  // The centroid gradients take one workgroup per (head, tile of 64
+  // centroids) and range of query blocks: enough ranges for about 1024
+  // workgroups, each of at least 8 query blocks, at most 16.
+  const long tiles = w.bh * w.nct;
+  long parts = (1024 + tiles - 1) / tiles;
+  parts = parts > 16 ? 16 : parts;
+  parts = parts > w.n / 8 ? w.n / 8 : parts;
+  b.cparts = parts < 1 ? 1 : (int)parts;
+  const size_t pbytes = b.cparts > 1 ? (size_t)b.cparts * w.bh * w.nct * 64 * s->D * sizeof(float) : 0;
+  b.dkbar_p = off;
+  off = align256(off + pbytes);
+  b.dvsum_p = off;
+  off = align256(off + pbytes);
   b.total = off;
   return b;
 }
@@ -508,6 +521,9 @@ PISA_API pisa_status_t pisa_attn_bwd(const pisa_shape_t* shape, const void* q, c
   a.dvsum = (float*)(base + bl.dvsum);
   a.kbt = base + bl.kbt;
   a.vbt = base + bl.vbt;
+  a.cparts = bl.cparts;
+  a.dkbar_p = (float*)(base + bl.dkbar_p);
+  a.dvsum_p = (float*)(base + bl.dvsum_p);
   a.L = shape->L;
   a.n = w.n;
   a.blk = shape->block;

@@ -102,13 +102,16 @@ struct BwdArgs {
   const float* lse_in;        // [BH][L]: ln D_t from the forward pass, or nullptr
   float *dkbar, *dvsum;       // [BH][n][D]: gradients of k̄_j and ΣV_j
   uint8_t *kbt, *vbt;         // [BH][nct*64][D]: k̄_j and ΣV_j in the I/O dtype, zero past n
+  float *dkbar_p, *dvsum_p;   // [cparts][BH][nct*64][D]: partial centroid gradients (cparts > 1)
+  int cparts;                 // query-block ranges the centroid gradients are split into
   int L, n, blk, n_last, nct, topk, W;
   float scale;
 };
 
 // Byte offsets of the backward workspace regions (all 256-aligned).
 struct BwdLayout {
-  size_t selmap, lse, delta, dkbar, dvsum, kbt, vbt, total;
+  size_t selmap, lse, delta, dkbar, dvsum, kbt, vbt, dkbar_p, dvsum_p, total;
+  int cparts;
 };
 
 enum StatsMode { kStatsFull = 0, kStatsMnorm = 1, kStatsPackOnly = 2 };
