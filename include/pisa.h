@@ -103,7 +103,9 @@ typedef struct {
  * squares in fp64; the spectral M_j sums the block's products in fp64.
  * The workspace: pisa_block_stats writes there the copies of K, V, k̄, ΣV and
  * H̄ in the I/O dtype, laid out in the operand order of the fused kernel, and
- * the largest key norms; pisa_select stages its routing scores there;
+ * the largest key norms; for rows of more than 1280 blocks pisa_select
+ * stages its routing scores there (shorter rows are scored and selected on
+ * chip);
  * pisa_attn_fwd reads the copies and resets and uses two counters there (the
  * tiles left to its running-maximum kernel, and the arrival count that keeps
  * its workgroups in step). A workspace therefore serves one call at a time:
@@ -147,7 +149,8 @@ pisa_status_t pisa_block_stats(const pisa_shape_t *shape, const void *q, const v
  * each query block's selection in ascending order.
  * Requires: 1 <= topk <= n; cov_weight >= 0 and finite; st->mnorm non-NULL
  * (computed by pisa_block_stats) when cov_weight > 0; the workspace of
- * pisa_block_stats (routing scores are staged there). */
+ * pisa_block_stats (the routing scores of rows longer than 1280 blocks are
+ * staged there). */
 pisa_status_t pisa_select(const pisa_shape_t *shape, const pisa_stats_t *st, double scale,
                           double cov_weight, int32_t topk, int32_t sink_idx, int32_t *idx,
                           void *stream);
@@ -203,7 +206,8 @@ pisa_status_t pisa_attn_fwd_lse(const pisa_shape_t *shape, const void *q, const 
  *   dq, dk, dv receive the gradients, shaped and typed like q, k, v
  *   ws        at least pisa_bwd_workspace_bytes(shape) bytes, 256-aligned:
  *             the selection as a bitmap, each row's log-sum of weights and
- *             Δ_t, and the fp32 gradients of k̄ and ΣV
+ *             Δ_t, and the fp32 gradients of k̄ and ΣV (for short sequences
+ *             also their partial sums over ranges of query blocks)
  * Products run on the matrix cores with fp32 accumulation; the weights and
  * their gradients are rounded to the I/O dtype as operands. Deterministic.
  * Errors as for pisa_attn_fwd. */
