@@ -339,7 +339,7 @@ __global__ __launch_bounds__(256) void k_topk_wave(TopkArgs a, long rows) {
 // wavefronts (the fp64 matrix cores reach about 35 TFLOP/s with one wavefront
 // per SIMD and 46-48 with two to four; measured on MI355X).
 // Phase 2: one wavefront per row selects on those 32 bits by a binary radix
-// select that counts with ballots (no LDS traffic). Where the k-th place falls
+// select that counts with wave-wide sums (no LDS traffic). Where the k-th place falls
 // inside a run of keys whose upper halves are equal and only part of the run
 // is taken (a near or exact tie), the wavefront forms the run's scores again,
 // bit for bit as before, and selects within the run on the lower 32 bits; keys
@@ -409,8 +409,21 @@ __device__ __forceinline__ uint32_t wave_or32(uint32_t x) {
 }
 __device__ __forceinline__ uint32_t wave_and32(uint32_t x) { return ~wave_or32(~x); }
 
+// Wave-wide sum of a 32-bit count through the same DPP steps: after each step
+// every lane holds the sum over twice as many lanes of its row of 16 (quads,
+// then half rows, then rows, each joined with its mirror image); the four rows'
+// sums are then added on the scalar side. The result is uniform.
+__device__ __forceinline__ int wave_sum32(int x) {
+  x += __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+  x += __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+  x += __builtin_amdgcn_mov_dpp(x, 0x141, 0xF, 0xF, false);  // row_half_mirror
+  x += __builtin_amdgcn_mov_dpp(x, 0x140, 0xF, 0xF, false);  // row_mirror
+  return __builtin_amdgcn_readlane(x, 0) + __builtin_amdgcn_readlane(x, 16) +
+         __builtin_amdgcn_readlane(x, 32) + __builtin_amdgcn_readlane(x, 48);
+}
+
 // MSB-first binary radix select over one wavefront's 32-bit keys (key[s] in
-// lane j % 64, slot j / 64), counting with ballots. cand (bit s: slot s of
+// lane j % 64, slot j / 64), counting with wave-wide sums. cand (bit s: slot s of
 // this lane) holds the candidates, ncand of them, of which the kk largest are
 // wanted. Each bit in which the candidates differ splits them: if at least kk
 // have it set, the rest drop out; otherwise all that have it are taken (sel)
@@ -430,15 +443,13 @@ __device__ __forceinline__ void ballot_select(const uint32_t (&key)[KPL], uint32
   while (diff != 0u && ncand > kk) {
     const int b = 31 - __clz(diff);
     diff &= ~(1u << b);
+    // the candidates with bit b set, gathered into one word per lane and
+    // counted with a single wave-wide sum
     uint32_t ones = 0u;
-    int cnt1 = 0;
 #pragma unroll
-    for (int s = 0; s < KPL; ++s) {
-      const uint32_t t = (key[s] >> b) & 1u;
-      ones |= t << s;
-      cnt1 += __popcll(__ballot((t & (cand >> s)) != 0u));
-    }
+    for (int s = 0; s < KPL; ++s) ones |= ((key[s] >> b) & 1u) << s;
     ones &= cand;
+    const int cnt1 = wave_sum32(__popc(ones));
     if (cnt1 >= kk) {
       cand = ones;
       ncand = cnt1;

@@ -379,8 +379,19 @@ __global__ __launch_bounds__(256) void k_hbar_reduce(StatsArgs a) {
   const int x = blockIdx.y * 256 + threadIdx.x;
   if (x < D * D) {
     const int d = x / D, e = x % D;
+    // the runs' partial sums in run order, loaded eight at a time so that the
+    // loads are in flight together
+    const float* hp = a.hpart + ((size_t)bh * a.nch * D + d) * D + e;
     double s = 0.0;
-    for (int c = 0; c < a.nch; ++c) s += (double)a.hpart[(((size_t)bh * a.nch + c) * D + d) * D + e];
+    int r = 0;
+    for (; r + 8 <= a.nch; r += 8) {
+      float x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) x[u] = hp[(size_t)(r + u) * D * D];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += (double)x[u];
+    }
+    for (; r < a.nch; ++r) s += (double)hp[(size_t)r * D * D];
     const double hbv = s / a.n;
     a.hbar[(bh * D + d) * D + e] = hbv;
     const int et = e >> 5, lane = ((d % (2 * KW)) / KW) * 32 + (e & 31), c = d / (2 * KW), ee = d % KW;
