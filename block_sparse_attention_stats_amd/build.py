@@ -16,6 +16,14 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libpisa.so")
 SOURCES = ["k_stats.hip", "k_mnorm.hip", "k_select.hip", "k_fwd.hip", "k_bwd.hip", "pisa_abi.hip"]
+# Translation units: (source, object name, extra flags). k_fwd.hip is built
+# twice: once for the bf16 fused pass and dense baseline with every MFMA result
+# in VGPRs (its weights then read the score accumulators without a move), once
+# the usual way for the rest (fp32, the per-block first-order variant).
+UNITS = [(src, src + ".o", []) for src in SOURCES] + [
+    ("k_fwd.hip", "k_fwd_bf16.hip.o",
+     ["-DPISA_FWD_VGPR_FORM=1", "-mllvm", "--amdgpu-mfma-vgpr-form=1"]),
+]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
@@ -25,9 +33,10 @@ FLAGS = [
 ]
 
 
-def _compile(src: str) -> str:
-    out = os.path.join(OBJ, src + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", out]
+def _compile(unit) -> str:
+    src, obj, extra = unit
+    out = os.path.join(OBJ, obj)
+    cmd = [HIPCC, *FLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", out]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")
@@ -86,8 +95,8 @@ def build_c_caller(verbose: bool = False) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OBJ, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
+    with cf.ThreadPoolExecutor(max_workers=len(UNITS)) as ex:
+        objs = list(ex.map(_compile, UNITS))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)

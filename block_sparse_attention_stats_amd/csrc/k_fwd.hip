@@ -256,11 +256,17 @@ __device__ __forceinline__ gbyte* sbase(const uint8_t* p) {
 }
 
 // One accumulator element into a VGPR, read where it is needed rather than as
-// part of a copy of the whole accumulator.
+// part of a copy of the whole accumulator. The unit of this file that is built
+// with every MFMA result in VGPRs (PISA_FWD_VGPR_FORM: the bf16 fused pass and
+// dense baseline) reads the value as it is, with no move.
 __device__ __forceinline__ float acc_read(float x) {
+#if PISA_FWD_VGPR_FORM
+  return x;
+#else
   float y;
   asm volatile("v_accvgpr_read_b32 %0, %1" : "=v"(y) : "a"(x));
   return y;
+#endif
 }
 
 template <int D, bool LAG, typename Wop>
@@ -1321,10 +1327,12 @@ __global__ __launch_bounds__(128, 1) void k_pisa_pb1_careful(FwdArgs a) {
   }
 }
 
+namespace {
 __global__ void k_zero_counters(int* redo, int* sync) {
   *redo = 0;
   *sync = 0;
 }
+}  // namespace
 
 template <typename T, int D, int SPB, bool DENSE>
 static hipError_t launch_fwd_t(const FwdArgs& a, hipStream_t s) {
@@ -1342,24 +1350,56 @@ static hipError_t launch_pb1_t(const FwdArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename T, int D>
-static hipError_t launch_fwd_b(FwdArgs a, hipStream_t s) {
+// Generations of resident workgroups: two 2-wave workgroups per CU.
+static hipError_t set_generation(FwdArgs& a) {
   int dev = 0, cus = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
   if (e != hipSuccess) return e;
-  a.nwg = 2L * cus < a.total ? 2L * cus : a.total;  // two resident 2-wave workgroups per CU
+  a.nwg = 2L * cus < a.total ? 2L * cus : a.total;
+  return hipSuccess;
+}
+
+#if PISA_FWD_VGPR_FORM
+// This unit of the file holds the bf16 fused pass and dense baseline only. It
+// is built with every MFMA result and accumulator in VGPRs, so the weights read
+// the Sᵀ accumulators directly; the unit built the usual way holds the rest.
+// Measured at the Wan shape on one box, same process: fused pass 15.37-15.43
+// -> 15.08 ms, dense baseline 95.0 -> 92.4 ms, same output bits.
+template <int D>
+static hipError_t launch_fused_bf16(FwdArgs a, hipStream_t s) {
+  hipError_t e = set_generation(a);
+  if (e != hipSuccess) return e;
+  const bool dense = a.idx == nullptr;
+  if (a.blk == 64)
+    return dense ? launch_fwd_t<bf16, D, 1, true>(a, s) : launch_fwd_t<bf16, D, 1, false>(a, s);
+  return dense ? launch_fwd_t<bf16, D, 2, true>(a, s) : launch_fwd_t<bf16, D, 2, false>(a, s);
+}
+
+hipError_t launch_fwd_bf16(int D, const FwdArgs& a, hipStream_t s) {
+  return D == 64 ? launch_fused_bf16<64>(a, s) : launch_fused_bf16<128>(a, s);
+}
+#else
+template <typename T, int D>
+static hipError_t launch_fwd_b(FwdArgs a, hipStream_t s) {
+  hipError_t e = set_generation(a);
+  if (e != hipSuccess) return e;
   const bool dense = a.idx == nullptr;
   if (a.per_block && !dense)
     return a.blk == 64 ? launch_pb1_t<T, D, 1>(a, s) : launch_pb1_t<T, D, 2>(a, s);
-  if (a.blk == 64)
-    return dense ? launch_fwd_t<T, D, 1, true>(a, s) : launch_fwd_t<T, D, 1, false>(a, s);
-  return dense ? launch_fwd_t<T, D, 2, true>(a, s) : launch_fwd_t<T, D, 2, false>(a, s);
+  if constexpr (sizeof(T) == 2) {
+    return launch_fwd_bf16(D, a, s);
+  } else {
+    if (a.blk == 64)
+      return dense ? launch_fwd_t<T, D, 1, true>(a, s) : launch_fwd_t<T, D, 1, false>(a, s);
+    return dense ? launch_fwd_t<T, D, 2, true>(a, s) : launch_fwd_t<T, D, 2, false>(a, s);
+  }
 }
 
 hipError_t launch_fwd(int dtype, int D, const FwdArgs& a, hipStream_t s) {
   if (dtype == 1) return D == 64 ? launch_fwd_b<bf16, 64>(a, s) : launch_fwd_b<bf16, 128>(a, s);
   return D == 64 ? launch_fwd_b<float, 64>(a, s) : launch_fwd_b<float, 128>(a, s);
 }
+#endif
 
 }  // namespace pisa

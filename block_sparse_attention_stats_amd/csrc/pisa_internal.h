@@ -128,6 +128,9 @@ hipError_t launch_route(int D, const RouteArgs& a, hipStream_t s);
 constexpr int kRouteMaxBlocks = 1280;  // longest row k_route keeps in LDS (80 KB per workgroup)
 // Fast pass, then the careful pass over the query tiles the fast pass queued.
 hipError_t launch_fwd(int dtype, int D, const FwdArgs& a, hipStream_t s);
+// The bf16 fused pass and dense baseline (not the per-block first-order
+// variant), from the unit of k_fwd.hip built with MFMA results in VGPRs.
+hipError_t launch_fwd_bf16(int D, const FwdArgs& a, hipStream_t s);
 
 // Backward of the zeroth-order variant: selection bitmap, dq (with the row
 // statistics), centroid gradients, then dk and dv.
