@@ -175,6 +175,25 @@ __device__ __forceinline__ void merge_halves(f32x16 (&acc)[DT], float* xf, int s
 // Both sweeps run over the same key tiles (the selected blocks' 64-key
 // sub-tiles, then the centroid tiles); the rows of tile u+1 load into
 // registers while tile u is computed.
+// The tile of workgroup wg in the XCD-aware order of the forward pass:
+// workgroups reach the chip's eight XCDs in turn, and within every full
+// generation of nwg workgroups those of one XCD take consecutive tiles of one
+// head, so the blocks they gather meet in that XCD's L2. A last, partial
+// generation keeps the plain order.
+__device__ __forceinline__ long bwd_tile_of(long wg, long nwg, long total) {
+  const long g = wg / nwg;
+  if ((g + 1) * nwg > total || (nwg & 7) != 0) return wg;
+  const long r = wg - g * nwg;
+  return g * nwg + (r & 7) * (nwg >> 3) + (r >> 3);
+}
+
+// k_bwd_dq runs in generations of as many workgroups as are resident, like the
+// forward pass: before its sweep a workgroup of generation g waits until every
+// workgroup of generation g-1 is past its selected sub-tiles, so the resident
+// ascending sweeps over the gathered blocks stay in step and one XCD's L2
+// serves each block to many of them. Every query tile has the same work (topk
+// blocks, then the centroid tiles). The wait is bounded by sync_ticks and
+// decides no result.
 template <typename T, int D, int SPB>
 __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
   using B = BT<T, D>;
@@ -189,13 +208,20 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
 
   const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5, l32 = lane & 31;
   const int w = tid >> 6, th = w & 1, xh = w >> 1;
-  const long item = blockIdx.x;
+  const long g = (long)blockIdx.x / a.nwg_dq;
+  const long item = bwd_tile_of(blockIdx.x, a.nwg_dq, a.total);
+  auto done = [&]() {
+    if (tid == 0) __hip_atomic_fetch_add(a.sync, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
   const int half = (int)(item % SPB);
   const long rest = item / SPB;
   const int i = (int)(rest % a.n);
   const long bh = rest / a.n;
   const int r0 = i * a.blk + half * 64;
-  if (r0 >= a.L) return;
+  if (r0 >= a.L) {
+    done();
+    return;
+  }
   const float cs = a.scale * kLog2e;
 
   const Rows krows = tensor_rows(a, a.k, bh), vrows = tensor_rows(a, a.v, bh);
@@ -229,7 +255,6 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
 
   // ln D_t from the forward pass makes the first sweep unnecessary
   const bool have_lse = a.lse_in != nullptr;
-  prefetch(0, have_lse);
   {
     uint4 pq[PER], po[PER];
     load_rows<T, D>(tensor_rows(a, a.q, bh), r0, pq);
@@ -256,6 +281,17 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
     acc += __shfl_xor(acc, 2);
     if (part == 0) dl_s[row] = acc;
   }
+  if (g > 0) {  // the generation wait
+    if (tid == 0) {
+      const int target = (int)(g * a.nwg_dq);
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__hip_atomic_load(a.sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < target &&
+             __builtin_amdgcn_s_memrealtime() - t0 < (uint64_t)a.sync_ticks)
+        __builtin_amdgcn_s_sleep(2);
+    }
+    __syncthreads();
+  }
+  prefetch(0, have_lse);
 
   // ---- sweep 1: log2 D_t with an online maximum (per lane: column t)
   float m = -kInf, l = 0.0f;
@@ -311,6 +347,7 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16{};
   for (int u = 0; u < ntile; ++u) {
+    if (u == nsub) done();  // past the selected sub-tiles: the centroid tiles follow
     __syncthreads();
     store_rows<T, D>(kt, pk);
     store_rows<T, D>(vt, pv);
@@ -390,8 +427,9 @@ __global__ __launch_bounds__(256, 2) void k_bwd_dkv(BwdArgs a) {
     i_lo = (int)((long)part * a.n / a.cparts);
     i_hi = (int)((long)(part + 1) * a.n / a.cparts);
   } else {
-    const int st = (int)(blockIdx.x % SPB);
-    const long rest = blockIdx.x / SPB;
+    const long item = bwd_tile_of(blockIdx.x, a.nwg_dkv, a.total);
+    const int st = (int)(item % SPB);
+    const long rest = item / SPB;
     j = (int)(rest % a.n);
     bh = rest / a.n;
     k0 = j * a.blk + st * 64;
@@ -595,14 +633,33 @@ __global__ void k_bwd_selmap_set(BwdArgs a) {
   }
 }
 
+__global__ void k_bwd_zero(int* x) { *x = 0; }
+
+// Workgroups of a kernel that can be resident at once, in multiples of the
+// eight XCDs (a generation of the XCD-aware order).
+template <typename K>
+static long resident_wgs(K kernel, long total) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess)
+    return total;
+  const long r = (long)(per_cu < 1 ? 1 : per_cu) * cus;
+  return r < total ? r : total;
+}
+
 template <typename T, int D, int SPB>
-hipError_t launch_bwd_t(const BwdArgs& a, long bh, hipStream_t s) {
+hipError_t launch_bwd_t(const BwdArgs& a0, long bh, hipStream_t s) {
+  BwdArgs a = a0;
+  a.nwg_dq = resident_wgs(k_bwd_dq<T, D, SPB>, a.total);
+  a.nwg_dkv = resident_wgs(k_bwd_dkv<T, D, SPB, false>, a.total);
   const size_t words = (size_t)bh * a.n * a.W;
   hipLaunchKernelGGL(k_bwd_selmap_clear, dim3(1024), dim3(256), 0, s, a.selmap, words);
   hipLaunchKernelGGL(k_bwd_selmap_set, dim3((unsigned)(bh * a.n)), dim3(256), 0, s, a);
   const long crow = bh * a.nct * 64;
   hipLaunchKernelGGL((k_bwd_prep<T, D>), dim3((unsigned)min(4096L, (crow * D + 255) / 256)), dim3(256), 0, s, a,
                      crow);
+  hipLaunchKernelGGL(k_bwd_zero, dim3(1), dim3(1), 0, s, a.sync);
   hipLaunchKernelGGL((k_bwd_dq<T, D, SPB>), dim3((unsigned)(bh * a.n * SPB)), dim3(256), 0, s, a);
   hipLaunchKernelGGL((k_bwd_dkv<T, D, SPB, true>), dim3((unsigned)(bh * a.nct * a.cparts)), dim3(256), 0, s, a);
   if (a.cparts > 1)

@@ -467,6 +467,8 @@ pisa::BwdLayout bwd_layout(const pisa_shape_t* s, const pisa::WsLayout& w) {
   off = align256(off + pbytes);
   b.dvsum_p = off;
   off = align256(off + pbytes);
+  b.sync = off;
+  off = align256(off + sizeof(int32_t));
   b.total = off;
   return b;
 }
@@ -532,6 +534,9 @@ PISA_API pisa_status_t pisa_attn_bwd(const pisa_shape_t* shape, const void* q, c
   a.topk = topk;
   a.W = (w.n + 31) / 32;
   a.scale = (float)scale;
+  a.sync = (int*)(base + bl.sync);
+  a.sync_ticks = 50000;  // 500 us, about one query tile's lifetime in k_bwd_dq at the Wan shape
+  a.total = w.bh * w.n * (shape->block / 64);
   return hip_status(pisa::launch_bwd(shape->dtype, shape->D, a, w.bh, (hipStream_t)stream));
 }
 

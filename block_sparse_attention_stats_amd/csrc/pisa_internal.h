@@ -106,11 +106,15 @@ struct BwdArgs {
   int cparts;                 // query-block ranges the centroid gradients are split into
   int L, n, blk, n_last, nct, topk, W;
   float scale;
+  int* sync;                  // k_bwd_dq's count of workgroups past their selected sub-tiles
+  int sync_ticks;             // longest wait at k_bwd_dq's generation barrier, 100 MHz ticks
+  long total;                 // query tiles (= key sub-tiles): bh * n * (blk / 64)
+  long nwg_dq, nwg_dkv;       // resident workgroups of k_bwd_dq / k_bwd_dkv (a generation)
 };
 
 // Byte offsets of the backward workspace regions (all 256-aligned).
 struct BwdLayout {
-  size_t selmap, lse, delta, dkbar, dvsum, kbt, vbt, dkbar_p, dvsum_p, total;
+  size_t selmap, lse, delta, dkbar, dvsum, kbt, vbt, dkbar_p, dvsum_p, sync, total;
   int cparts;
 };
 
