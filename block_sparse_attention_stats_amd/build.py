@@ -19,10 +19,13 @@ SOURCES = ["k_stats.hip", "k_mnorm.hip", "k_select.hip", "k_fwd.hip", "k_bwd.hip
 # Translation units: (source, object name, extra flags). k_fwd.hip is built
 # twice: once for the bf16 fused pass and dense baseline with every MFMA result
 # in VGPRs (its weights then read the score accumulators without a move), once
-# the usual way for the rest (fp32, the per-block first-order variant).
-UNITS = [(src, src + ".o", []) for src in SOURCES] + [
+# the usual way for the rest (fp32, the per-block first-order variant). The
+# backward kernels are built with MFMA results in VGPRs too: k_bwd_dq then
+# keeps two tiles of rows in flight at two wavefronts per SIMD.
+VGPR_FORM = ["-mllvm", "--amdgpu-mfma-vgpr-form=1"]
+UNITS = [(src, src + ".o", VGPR_FORM if src == "k_bwd.hip" else []) for src in SOURCES] + [
     ("k_fwd.hip", "k_fwd_bf16.hip.o",
-     ["-DPISA_FWD_VGPR_FORM=1", "-mllvm", "--amdgpu-mfma-vgpr-form=1"]),
+     ["-DPISA_FWD_VGPR_FORM=1", *VGPR_FORM]),
 ]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -235,11 +235,12 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
     return 64 * (u - nsub);
   };
   uint4 pk[PER], pv[PER];
-  auto prefetch = [&](int u, bool values) {
+  auto prefetch_into = [&](int u, bool values, uint4 (&xk)[PER], uint4 (&xv)[PER]) {
     const int k0 = tile_r0(u);
-    load_rows<T, D>(u < nsub ? krows : kbrows, k0, pk);
-    if (values) load_rows<T, D>(u < nsub ? vrows : vbrows, k0, pv);
+    load_rows<T, D>(u < nsub ? krows : kbrows, k0, xk);
+    if (values) load_rows<T, D>(u < nsub ? vrows : vbrows, k0, xv);
   };
+  auto prefetch = [&](int u, bool values) { prefetch_into(u, values, pk, pv); };
   // weight of each key of tile u: 1 for a token, n_j for an unselected
   // centroid, -1 for no key (past the sequence, padding, selected centroid)
   auto set_weights = [&](int u) {
@@ -342,18 +343,26 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
     }
   }
 
-  // ---- sweep 2: dq_t = s Σ_x dS_tx K_x
+  // ---- sweep 2: dq_t = s Σ_x dS_tx K_x. The rows of two tiles are in flight
+  // in registers (tiles u+1 and u+2 load while tile u is computed), so a
+  // gathered block that misses the L2 has two tiles' compute to arrive. Built
+  // with every MFMA result in VGPRs this takes 237 registers per lane (bf16,
+  // D = 128), two wavefronts per SIMD; built with the accumulators in AGPRs it
+  // takes 292, one wavefront per SIMD, and the backward ran 90.0 -> 110.7 ms
+  // at the Wan shape instead of 90.0 -> 87.2 ms.
   f32x16 dq[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) dq[dt] = f32x16{};
-  for (int u = 0; u < ntile; ++u) {
+  uint4 pk2[PER], pv2[PER];
+  if (ntile > 1) prefetch_into(1, true, pk2, pv2);
+  auto tile = [&](int u, uint4 (&xk)[PER], uint4 (&xv)[PER]) {
     if (u == nsub) done();  // past the selected sub-tiles: the centroid tiles follow
     __syncthreads();
-    store_rows<T, D>(kt, pk);
-    store_rows<T, D>(vt, pv);
+    store_rows<T, D>(kt, xk);
+    store_rows<T, D>(vt, xv);
     set_weights(u);
     __syncthreads();
-    if (u + 1 < ntile) prefetch(u + 1, true);
+    if (u + 2 < ntile) prefetch_into(u + 2, true, xk, xv);
     f32x16 sacc = f32x16{}, pacc = f32x16{};
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
@@ -375,6 +384,10 @@ __global__ __launch_bounds__(256, 1) void k_bwd_dq(BwdArgs a) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) Op<T>::mma(dq[dt], av, op_col<T, D>(kt, xh, dt, c, lane));
     }
+  };
+  for (int u = 0; u < ntile; u += 2) {
+    tile(u, pk, pv);
+    if (u + 1 < ntile) tile(u + 1, pk2, pv2);
   }
   __syncthreads();
   merge_halves<DT>(dq, (float*)kv, th, xh, lane);
