@@ -206,8 +206,11 @@ pisa_status_t pisa_attn_fwd_lse(const pisa_shape_t *shape, const void *q, const 
  *   dq, dk, dv receive the gradients, shaped and typed like q, k, v
  *   ws        at least pisa_bwd_workspace_bytes(shape) bytes, 256-aligned:
  *             the selection as a bitmap, each row's log-sum of weights and
- *             Δ_t, and the fp32 gradients of k̄ and ΣV (for short sequences
- *             also their partial sums over ranges of query blocks)
+ *             Δ_t, the fp32 gradients of k̄ and ΣV (for short sequences
+ *             also their partial sums over ranges of query blocks), and a
+ *             counter, reset by each call, that keeps the dq workgroups in
+ *             step; a workspace serves one call at a time (order calls that
+ *             share one, e.g. on one stream)
  * Products run on the matrix cores with fp32 accumulation; the weights and
  * their gradients are rounded to the I/O dtype as operands. Deterministic.
  * Errors as for pisa_attn_fwd. */
