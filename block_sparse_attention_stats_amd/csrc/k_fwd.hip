@@ -337,6 +337,21 @@ __device__ __forceinline__ void xstep(typename Regs<bf16, D>::Acc& oacc,
       py[qt][c] = make_uint4(pw[qt][4 * c], pw[qt][4 * c + 1], pw[qt][4 * c + 2], pw[qt][4 * c + 3]);
 }
 
+// Start values of the 16 Sᵀ accumulator elements of a lane from a bit mask of
+// its keys (bit vkey(r, 0) set: key r takes no weight): −inf or 0. The bit,
+// sign-extended and shifted into the exponent field, gives 0xFF800000 (−inf)
+// or 0 in two integer operations, with no compare, no condition register, and
+// none of the wait states a condition select needs before an MFMA reads it.
+__device__ __forceinline__ f32x16 dead_init(uint32_t dh) {
+  f32x16 v;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int s = (int)(dh << (31 - vkey(r, 0))) >> 31;  // 0 or -1
+    v[r] = __builtin_bit_cast(float, (uint32_t)s << 23);
+  }
+  return v;
+}
+
 // Keys of a wavefront's 32 that lie past the end of the sequence, as a bit
 // mask (bit k: key k), given how many of them are valid.
 __device__ __forceinline__ uint32_t dead_keys(int nvalid) {
@@ -724,9 +739,7 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
           const int jbase = kSub * ct + 32 * w;
           const int nvalid = a.n - jbase;  // valid centroids from this wavefront's first key
           const uint32_t dh = (sh.selmask[jbase >> 5] | dead_keys(nvalid)) >> (4 * h);
-          f32x16 v;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) v[r] = ((dh >> vkey(r, 0)) & 1u) ? kNegInf : 0.0f;
+          const f32x16 v = dead_init(dh);
           return v;
         };
         pipelined<T, D, true, false>(
@@ -782,9 +795,7 @@ __device__ __forceinline__ void query_tile(const FwdArgs& a, long item, FwdShare
     auto init = [&](int t) {
       const uint32_t dh =
           (t < nt_full ? 0u : dead_keys(a.n_last - kSub * (t - nt_full) - 32 * w)) >> (4 * h);
-      f32x16 v;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = ((dh >> vkey(r, 0)) & 1u) ? kNegInf : 0.0f;
+      const f32x16 v = dead_init(dh);
       return v;
     };
     pipelined<T, D, true, true>(
@@ -1062,8 +1073,7 @@ __device__ __forceinline__ void pb1_tile(const FwdArgs& a, long item, FwdShared<
     f32x16 v = f32x16{};
     if (ragged && g >= g_last) {
       const uint32_t dh = dead_keys(a.n_last - kSub * (g - g_last) - 32 * w) >> (4 * h);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = ((dh >> vkey(r, 0)) & 1u) ? kNegInf : 0.0f;
+      v = dead_init(dh);
     }
     return v;
   };
@@ -1135,9 +1145,7 @@ __device__ __forceinline__ void pb1_tile(const FwdArgs& a, long item, FwdShared<
     auto init = [&](int t) {
       const uint32_t dh =
           (t < nt_full ? 0u : dead_keys(a.n_last - kSub * (t - nt_full) - 32 * w)) >> (4 * h);
-      f32x16 v;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = ((dh >> vkey(r, 0)) & 1u) ? kNegInf : 0.0f;
+      const f32x16 v = dead_init(dh);
       return v;
     };
     pipelined<T, D, true, true>(nt, a.kp, a.vp, off, [](int) { return f32x16{}; }, init, l, m, cs, qr,
