@@ -67,7 +67,7 @@ pisa_status_t check_shape(const pisa_shape_t* s, pisa::WsLayout* w) {
   w->redo = off;
   off = align256(off + ((size_t)bh * n * w->spb + 1) * sizeof(int32_t));
   w->sync = off;
-  off = align256(off + sizeof(int32_t));
+  off = align256(off + pisa::kSyncCounters * sizeof(int32_t));
   w->dense_total = off;
   w->kbp = off;
   off = align256(off + (size_t)bh * w->nct * sub);

@@ -17,7 +17,7 @@ struct WsLayout {
                       // n <= kRouteMaxBlocks (k_route keeps them on chip)
   size_t kmax2;       // fp32 largest squared key norm per run of blocks: [BH][nch]
   size_t redo;        // int32 count + list of query tiles the careful kernel recomputes
-  size_t sync;        // int32 arrival counter of the fast kernel's generation barrier
+  size_t sync;        // int32 arrival counters of the fast kernel's generation barrier, one per XCD
   size_t total;       // bytes needed by stats + select + forward
   size_t dense_total; // bytes needed by the dense baseline (kp + vp)
   int n, spb, nct, cb, nch, esz;
@@ -72,7 +72,7 @@ struct FwdArgs {
   const int32_t* idx;  // nullptr: every key block (dense)
   const float* kmax2;  // [BH][nch] largest squared key norm per run of blocks
   int* redo;           // [0]: count, [1..]: query tiles left to the careful kernel
-  int* sync;           // arrival counter of the generation barrier of the fast kernel
+  int* sync;           // arrival counters of the fast kernel's generation barrier (kSyncCounters)
   long nwg;            // workgroups per generation of the fast kernel (as many as are resident)
   int sync_ticks;      // longest wait at a generation barrier, in 100 MHz ticks
   long total;
@@ -140,6 +140,7 @@ hipError_t launch_fwd_bf16(int D, const FwdArgs& a, hipStream_t s);
 // statistics), centroid gradients, then dk and dv.
 hipError_t launch_bwd(int dtype, int D, const BwdArgs& a, long bh, hipStream_t s);
 
+constexpr int kSyncCounters = 8;  // one generation-barrier counter per XCD
 constexpr int kMaxBlocks = 8192;  // routing keeps one score row per workgroup in LDS
 
 }  // namespace pisa
