@@ -291,6 +291,25 @@ __device__ __forceinline__ void xstep(typename Regs<bf16, D>::Acc& oacc,
   // base, which issues faster than a 64-bit address per lane
   uint32_t lane_off = (uint32_t)lane * 16u;
   asm volatile("" : "+v"(lane_off));  // keeps base + lane offset from being hoisted as one 64-bit value
+  // The addresses of this wavefront's part of the next V and K sub-tiles,
+  // chunk x at x KiB, every load in the scalar-base form (uniform base plus a
+  // 32-bit lane offset). Built with the accumulators in AGPRs (the per-block
+  // first-order variant) one base per four chunks serves, the chunk offset
+  // within them going to the load's immediate: 36 scalar instructions fewer per
+  // 64 MFMAs, pb1 108.2-108.6 -> 103.9-104.0 ms. In the VGPR-form unit each
+  // chunk keeps a base of its own: there the shared bases measured the fused
+  // pass 1% slower (Wan 14.83-14.89 -> 15.00-15.03 ms), in one process.
+#if PISA_FWD_VGPR_FORM
+  auto vaddr = [&](int x) { return sbase(vnext + (size_t)((w * NV + x) * kWave * 16)); };
+  auto kaddr = [&](int c) { return sbase(knext + (size_t)((w * G::NC + c) * kWave * 16)); };
+#else
+  gbyte* const vb[2] = {sbase(vnext + (size_t)(w * NV) * kWave * 16),
+                        sbase(vnext + (size_t)(w * NV + 4) * kWave * 16)};
+  gbyte* const kb[2] = {sbase(knext + (size_t)(w * G::NC) * kWave * 16),
+                        sbase(knext + (size_t)(w * G::NC + 4) * kWave * 16)};
+  auto vaddr = [&](int x) { return vb[x >> 2] + (x & 3) * kWave * 16; };
+  auto kaddr = [&](int c) { return kb[c >> 2] + (c & 3) * kWave * 16; };
+#endif
   sx[0] = init;
   sx[1] = init;
   // With LAG the weights run as a three-stage pipeline over the 32 elements, so
@@ -309,12 +328,12 @@ __device__ __forceinline__ void xstep(typename Regs<bf16, D>::Acc& oacc,
       const int x = mi >> 1, qt = mi & 1;
       Op<bf16>::mma(oacc[x / G::CPK][qt], vc[x], pc[qt][x % G::CPK]);
       if (qt == 1)
-        vc[x] = __builtin_bit_cast(uint4, *(gu32x4*)(sbase(vnext + (size_t)((w * NV + x) * kWave * 16)) + lane_off));
+        vc[x] = __builtin_bit_cast(uint4, *(gu32x4*)(vaddr(x) + lane_off));
     } else if (mi < NM) {
       const int c = (mi - NPV) >> 1, qt = (mi - NPV) & 1;
       Op<bf16>::mma(sx[qt], kc[c], qr[qt][c]);
       if (qt == 1)
-        kc[c] = __builtin_bit_cast(uint4, *(gu32x4*)(sbase(knext + (size_t)((w * G::NC + c) * kWave * 16)) + lane_off));
+        kc[c] = __builtin_bit_cast(uint4, *(gu32x4*)(kaddr(c) + lane_off));
     }
 #pragma unroll
     for (int u = 0; u < EPM; ++u) {
