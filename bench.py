@@ -37,9 +37,9 @@ HBM_PEAK_GBS = 8000.0
 # is kept, and the figure is reported as null once the sources differ.
 FUSED_TRAFFIC = {"workload": "wan_bf16",
                  "sources": ["k_fwd.hip", "pisa_dev.h", "pisa_internal.h", "pisa_abi.hip"],
-                 "sha1": "97f6f7e6bec2f51acd4b1ad62c2b00a758d22016",
-                 "fetch_kib": (27688166.6 + 28002869.0) / 2, "fetch_scale": 2.0,
-                 "write_kib": (828397.9 + 828398.6) / 2, "write_scale": 1.0}
+                 "sha1": "8e04eef5caf51e152ec29ca28b273729e03d871c",
+                 "fetch_kib": (28095046.7 + 28225541.3) / 2, "fetch_scale": 2.0,
+                 "write_kib": (828397.9 + 828397.6) / 2, "write_scale": 1.0}
 
 
 def fused_traffic(workload: str):
